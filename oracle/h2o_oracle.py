@@ -1,0 +1,243 @@
+"""Plain float64 CPU oracle of the Heavy-Hitter Oracle (H2O) fixed-budget KV cache.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import or run anything under ``oracle/``. The product path
+(the HIP library and its Python binding) never does, and the two share no
+code: the only thing both consume is the seeded input generator in
+``workload/``, which holds none of the method's arithmetic.
+
+Citations
+---------
+"H2O §x" means the page "H2O: Heavy-Hitter Oracle for Efficient Generative
+Inference of Large Language Models" (the paperlayer.ai source-linked summary
+of arXiv 2306.14048v3), section x and the bullet named after it.
+
+What is computed (per (batch, head), independently, all in float64)
+------------------------------------------------------------------
+Prefill over a prompt of n tokens:
+  P[i, j] = softmax over j <= i of scale * <Q_i, K_j>   (H2O §D "Recursive attention")
+  c_j     = sum_i P[i, j]                                (accumulated attention, H2O §1, §4.1)
+  keep all n tokens when n <= k; otherwise keep the k_recent newest positions
+  and the k_heavy candidates in [0, n - k_recent) with the largest (c_j, j)
+  (H2O §A "Pseudocode", "System Details").
+Decode step at position t:
+  attend over the cached tokens plus the new token itself (H2O §D, attention is
+  taken over the prefix including row t, before eviction); add each cached
+  token's probability to its score (accumulated, not averaged: H2O §B.2
+  "Previous Attempts"); when the cache is full, evict the eligible slot with
+  the smallest (score, pos), where eligible means pos <= t - k_recent
+  (at most one eviction per step, fixed size k: H2O §2 "Problem formulation",
+  §D "Cache eviction"); write the new token into the freed slot with score
+  p_new.
+
+Readings where the page is silent (the design notes list them all):
+  self-attention of the new token is included; accumulation happens before the
+  victim is chosen; the recent window is (t - k_recent, t]; the new token's
+  initial score is its own probability; ties are broken by the total order
+  (score, pos); prefill candidates exclude the recent window; the slot layout is
+  heavy positions ascending in slots [0, k_heavy), recent positions ascending in
+  [k_heavy, k), and a decode step writes into the victim's slot (or slot n_used
+  while the cache is not yet full).
+
+Pins: brute force on tiny inputs, the q = 0 closed form, textbook special
+cases (full cache = causal attention, k_heavy = 0 = sliding window), the
+budget-3 illustration of H2O §4.1 and invariants; see tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = ["causal_attention_probs", "prefill_column_sums", "select_prefill",
+           "eligible_slots", "choose_victim", "H2OOracle", "PrefillResult", "StepResult"]
+
+
+def causal_attention_probs(Q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
+    """Row-softmax attention of every prompt query over the keys up to its own position.
+
+    H2O §D "Recursive attention": query row i attends over the first i key rows
+    (its own included) and is normalised by that row's own sum D_i.
+    Returns P with P[i, j] = 0 for j > i.
+    """
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    n = Q.shape[0]
+    S = scale * (Q @ K.T)
+    S = np.where(np.tril(np.ones((n, n), dtype=bool)), S, -np.inf)
+    E = np.exp(S - S.max(axis=1, keepdims=True))
+    return E / E.sum(axis=1, keepdims=True)
+
+
+def prefill_column_sums(Q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
+    """c_j: total normalised attention that prompt token j receives from all prompt queries.
+
+    This is the accumulated attention statistic of H2O §1 ("Greedy algorithm for
+    low-cost policy") and §4.1, taken over the whole prompt (diagonal included).
+    """
+    if np.asarray(Q).shape[0] == 0:
+        return np.zeros(0, np.float64)
+    return causal_attention_probs(Q, K, scale).sum(axis=0)
+
+
+def select_prefill(c: np.ndarray, k_heavy: int, k_recent: int):
+    """Positions kept after prefill, in slot order, and the selection margin.
+
+    H2O §A "Pseudocode": a prompt long enough is reduced to heavy hitters plus
+    recent tokens; §A "System Details": heavy hitters first, recent tokens last.
+    Candidates for the heavy part are the positions before the recent window.
+    Keys compare as (c_j, j), so on equal scores the later position is kept.
+    The margin is the relative gap between the smallest kept candidate score
+    and the largest dropped one (inf when nothing is dropped).
+    """
+    c = np.asarray(c, np.float64)
+    n = c.shape[0]
+    k = k_heavy + k_recent
+    if n <= k:
+        return np.arange(n, dtype=np.int64), np.inf
+    recent = np.arange(n - k_recent, n, dtype=np.int64)
+    candidates = list(range(n - k_recent))
+    ranked = sorted(candidates, key=lambda j: (c[j], j), reverse=True)
+    heavy = np.array(sorted(ranked[:k_heavy]), dtype=np.int64)
+    margin = np.inf
+    if 0 < k_heavy < len(ranked):
+        lo_kept, hi_dropped = c[ranked[k_heavy - 1]], c[ranked[k_heavy]]
+        margin = (lo_kept - hi_dropped) / lo_kept if lo_kept > 0 else 0.0
+    return np.concatenate([heavy, recent]), margin
+
+
+def eligible_slots(pos: np.ndarray, t: int, k_recent: int) -> np.ndarray:
+    """Slots that may be evicted at step t: those outside the recent window (t - k_recent, t].
+
+    H2O §A "System Details" keeps the newest tokens in a recent region; with the
+    new token t counted in it, a slot is evictable iff pos <= t - k_recent.
+    """
+    return (pos >= 0) & (pos <= t - k_recent)
+
+
+def choose_victim(score: np.ndarray, pos: np.ndarray, eligible: np.ndarray):
+    """Per head, the eligible slot with the smallest (score, pos), and the eviction margin.
+
+    H2O §4.1 and §D "Cache eviction": the lowest accumulated score leaves.
+    Ties on the score evict the older position. The margin is
+    (second smallest - smallest) / second smallest over the eligible scores.
+    """
+    G = score.shape[0]
+    masked = np.where(eligible, score, np.inf)
+    smallest = masked.min(axis=1)
+    tied = eligible & (score == smallest[:, None])
+    victim = np.argmin(np.where(tied, pos, np.iinfo(np.int64).max), axis=1)
+    margin = np.full(G, np.inf)
+    for g in range(G):
+        e = np.sort(score[g][eligible[g]])
+        if e.size >= 2:
+            margin[g] = (e[1] - e[0]) / e[1] if e[1] > 0 else 0.0
+    return victim, margin
+
+
+@dataclass
+class PrefillResult:
+    colsum: np.ndarray   # [G, n] float64 prompt column sums
+    margin: np.ndarray   # [G] selection margin (inf = unique by construction)
+
+
+@dataclass
+class StepResult:
+    out: np.ndarray      # [G, d] attention output of the new query
+    evicted: np.ndarray  # [G] evicted position, -1 when nothing was evicted
+    margin: np.ndarray   # [G] eviction margin (inf when nothing was evicted)
+    probs: np.ndarray    # [G, n_used + 1] probabilities over the cached slots then the new token
+    slot: np.ndarray     # [G] slot the new token was written into
+
+
+class H2OOracle:
+    """fp64 state of G independent (batch, head) caches with k = k_heavy + k_recent slots.
+
+    State per head: K, V rows per slot, the accumulated score per slot, the
+    position each slot holds (-1 = empty), plus the shared counters n_used (the
+    number of occupied slots, always min(k, t)) and t (position of the next
+    token). Slots [0, n_used) are the occupied ones.
+    """
+
+    def __init__(self, n_heads: int, head_dim: int, k_heavy: int, k_recent: int, scale: float):
+        if k_heavy < 0 or k_recent < 1:
+            raise ValueError("need k_heavy >= 0 and k_recent >= 1")
+        self.G, self.d = n_heads, head_dim
+        self.k_heavy, self.k_recent = k_heavy, k_recent
+        self.k = k_heavy + k_recent
+        self.scale = float(scale)
+        self.K = np.zeros((self.G, self.k, self.d))
+        self.V = np.zeros((self.G, self.k, self.d))
+        self.score = np.zeros((self.G, self.k))
+        self.pos = np.full((self.G, self.k), -1, dtype=np.int64)
+        self.n_used = 0
+        self.t = 0
+
+    def prefill(self, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> PrefillResult:
+        """Score the prompt and seed the cache (H2O §A "Pseudocode"); Q, K, V are [G, n, d]."""
+        Q = np.asarray(Q, np.float64)
+        K = np.asarray(K, np.float64)
+        V = np.asarray(V, np.float64)
+        n = Q.shape[1]
+        colsum = np.zeros((self.G, n))
+        margin = np.full(self.G, np.inf)
+        self.score[:] = 0.0
+        self.pos[:] = -1
+        self.K[:] = 0.0
+        self.V[:] = 0.0
+        for g in range(self.G):
+            colsum[g] = prefill_column_sums(Q[g], K[g], self.scale)
+            keep, margin[g] = select_prefill(colsum[g], self.k_heavy, self.k_recent)
+            m = keep.size
+            self.pos[g, :m] = keep
+            self.score[g, :m] = colsum[g][keep]
+            self.K[g, :m] = K[g][keep]
+            self.V[g, :m] = V[g][keep]
+        self.n_used = min(n, self.k)
+        self.t = n
+        return PrefillResult(colsum, margin)
+
+    def decode_step(self, q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray) -> StepResult:
+        """One decode step for every head; q, k_new, v_new are [G, d].
+
+        Order (H2O §D "Recursive attention" then "Cache eviction"): attend over
+        the cache plus the new token, accumulate the probabilities into the
+        scores, then evict at most one slot and store the new token.
+        """
+        q = np.asarray(q, np.float64)
+        k_new = np.asarray(k_new, np.float64)
+        v_new = np.asarray(v_new, np.float64)
+        nu, G = self.n_used, self.G
+        Kc, Vc = self.K[:, :nu], self.V[:, :nu]
+
+        logits = np.concatenate(
+            [self.scale * np.einsum("gkd,gd->gk", Kc, q),
+             self.scale * np.einsum("gd,gd->g", k_new, q)[:, None]], axis=1)
+        e = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        out = np.einsum("gk,gkd->gd", p[:, :nu], Vc) + p[:, nu:nu + 1] * v_new
+
+        self.score[:, :nu] += p[:, :nu]
+
+        if nu < self.k:
+            slot = np.full(G, nu, dtype=np.int64)
+            evicted = np.full(G, -1, dtype=np.int64)
+            margin = np.full(G, np.inf)
+            self.n_used = nu + 1
+        else:
+            elig = eligible_slots(self.pos, self.t, self.k_recent)
+            slot, margin = choose_victim(self.score, self.pos, elig)
+            evicted = self.pos[np.arange(G), slot].copy()
+
+        rows = np.arange(G)
+        self.K[rows, slot] = k_new
+        self.V[rows, slot] = v_new
+        self.pos[rows, slot] = self.t
+        self.score[rows, slot] = p[:, nu]
+        self.t += 1
+        return StepResult(out, evicted, margin, p, slot)
+
+    def snapshot(self) -> dict:
+        """Copy of the full state (used to resync another implementation)."""
+        return dict(K=self.K.copy(), V=self.V.copy(), score=self.score.copy(),
+                    pos=self.pos.copy(), n_used=self.n_used, t=self.t)
