@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Throughput of the H2O hot path on one MI355X.
+
+One benchmark step is one pass of the whole path over one batch: for every
+layer cache, clear it, score and select the prompt (prefill), then run all
+decode steps (attention + score accumulation + one eviction + insert per
+step). Several independent layer caches are decoded in rotation, token step
+by token step, as a model's layers would be, so that no cache is re-read out
+of the 256 MB Infinity Cache between its own steps. Inputs are synthetic and
+resident in HBM before the timed region starts.
+
+Prints ONE JSON line. ``value`` is decode head-steps per second over the
+whole step (prefill included); the roofline object grades the dominant
+kernel (the fused decode step) against the 8 TB/s HBM peak; the CPU baseline
+is the fp64 oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
+METRIC = "H2O decode head-steps/sec + achieved HBM GB/s (% of MI355X peak)"
+DECODE_SOURCES = ["decode.hip", "h2o_device.h", "launch.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="opt6.7b_layer")
+    p.add_argument("--layers", type=int, default=4, help="independent layer caches decoded in rotation")
+    p.add_argument("--cpu-heads", type=int, default=256, help="heads in the CPU-oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-single-layer", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run a plain 1 GiB device copy first (scale factor for HBM counters)")
+    return p.parse_args()
+
+
+def decode_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "kv_cache_eviction_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes_per_head(n_used: int, d: int, e: int) -> int:
+    """Algorithmic HBM bytes of one fused decode step for one (batch, head).
+
+    reads: K and V rows of the occupied slots, score and pos of every
+    occupied slot, q, k_new, v_new; writes: every occupied score, the output
+    row (fp32), the new K and V rows, the new slot's pos, the evicted position.
+    """
+    return 2 * n_used * d * e + 12 * n_used + 5 * d * e + 4 * d + 8
+
+
+def load_traffic(workload: str, digest: str):
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, heads: int):
+    """The fp64 oracle on a bounded sample: `heads` heads, prefill plus every decode step."""
+    import numpy as np
+    from oracle import H2OOracle
+    from workload import make_decode, make_prompt, sample_heads
+
+    sample = sample_heads(wl, heads, seed=11)
+    Q, K, V = make_prompt(wl, heads=sample)
+    q, k, v = make_decode(wl, heads=sample)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    orc = H2OOracle(sample.size, wl.head_dim, wl.k_heavy, wl.k_recent, wl.scale)
+    t0 = time.perf_counter()
+    orc.prefill(Q, K, V)
+    t1 = time.perf_counter()
+    for t in range(wl.steps):
+        orc.decode_step(q[:, t], k[:, t], v[:, t])
+    t2 = time.perf_counter()
+    del np
+    return {
+        "value": sample.size * wl.steps / (t2 - t0),
+        "unit": "head-steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{sample.size} of {wl.n_heads_total} heads, full prompt {wl.prompt_len} prefill + "
+                   f"{wl.steps} decode steps, fp64 numpy (prefill {t1 - t0:.2f} s, decode {t2 - t1:.2f} s)"),
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the H2O path shards by (batch, head) with no communication, so a multi-GPU run "
+              "is the same kernel on each GPU's share and is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cache_eviction_decode_amd import H2OCache, load_library
+    from workload import ELEM_BYTES, WORKLOADS, make_decode, make_prompt
+
+    lib = load_library()
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
+    B, H, d, n, T, L = wl.batch, wl.heads, wl.head_dim, wl.prompt_len, wl.steps, args.layers
+    G, k, e = wl.n_heads_total, wl.k, ELEM_BYTES[wl.dtype]
+    log(f"[bench] {wl.describe()}; {L} layer caches")
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+
+    t_gen = time.perf_counter()
+    Qh, Kh, Vh = make_prompt(wl)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(tdt)
+    Q, K, V = (up(x).view(B, H, n, d) for x in (Qh, Kh, Vh))
+    del Qh, Kh, Vh
+    qh, kh, vh = make_decode(wl)
+    qs, ks, vs = (up(x.transpose(1, 0, 2)).view(T, B, H, d) for x in (qh, kh, vh))
+    del qh, kh, vh
+    log(f"[bench] inputs generated and resident in HBM ({time.perf_counter() - t_gen:.1f} s)")
+
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    caches = [H2OCache(B, H, d, wl.k_heavy, wl.k_recent, tdt, wl.scale, dev) for _ in range(L)]
+    ws = caches[0].workspace(n)
+    outs = [torch.empty(B, H, d, dtype=torch.float32, device=dev) for _ in range(L)]
+    evs = [torch.empty(B, H, dtype=torch.int32, device=dev) for _ in range(L)]
+    qp = [qs[t].data_ptr() for t in range(T)]
+    kp = [ks[t].data_ptr() for t in range(T)]
+    vp = [vs[t].data_ptr() for t in range(T)]
+    dcode = {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype]
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(lib.h2o_last_error().decode())
+
+    def run_step(layers, ev=None):
+        """Whole path for `layers` caches: clear, prefill, T decode steps."""
+        for i in layers:
+            c = caches[i]
+            check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, dcode,
+                                     ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
+                                     c.score.data_ptr(), c.pos.data_ptr(), sh))
+            check(lib.h2o_prefill_select(ctypes.byref(c.desc), Q.data_ptr(), K.data_ptr(), V.data_ptr(), n,
+                                         ws.data_ptr(), ws.numel(), None, sh))
+        if ev is not None:
+            ev.record(stream)
+        for t in range(T):
+            for i in layers:
+                check(lib.h2o_decode_step(ctypes.byref(caches[i].desc), qp[t], kp[t], vp[t],
+                                          outs[i].data_ptr(), evs[i].data_ptr(), sh))
+
+    all_layers = list(range(L))
+    for _ in range(args.warmup):
+        run_step(all_layers)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for s in range(args.steps):
+        starts[s].record(stream)
+        run_step(all_layers, mids[s])
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - w0
+    step_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
+    prefill_ms = [starts[s].elapsed_time(mids[s]) for s in range(args.steps)]
+    decode_ms = [mids[s].elapsed_time(ends[s]) for s in range(args.steps)]
+    ms_per_step = sum(step_ms) / args.steps
+    head_steps = G * T * L
+    value = head_steps / (ms_per_step / 1e3)
+
+    n_used = [min(k, n + t) for t in range(T)]
+    bytes_per_launch = G * sum(decode_bytes_per_head(u, d, e) for u in n_used) / T
+    launches = T * L
+    avg_launch_s = (sum(decode_ms) / args.steps) / 1e3 / launches
+    achieved = bytes_per_launch / avg_launch_s / 1e9
+    digest = decode_source_digest()
+    traffic = load_traffic(wl.name, digest)
+    prefill_flops = 2.0 * n * (n + 1) * d * G  # two causal QK^T passes per layer
+    pf_s = (sum(prefill_ms) / args.steps) / 1e3 / L
+
+    single = None
+    if not args.no_single_layer and L > 1:
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for s in range(2):
+            e0[s].record(stream)
+            run_step([0], e1[s])
+        e2 = torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        dms = e1[1].elapsed_time(e2)
+        single = {"decode_us_per_launch": dms * 1e3 / T,
+                  "decode_GBps": bytes_per_launch / (dms / 1e3 / T) / 1e9,
+                  "note": "one cache decoded alone: its 268 MB are partly re-read from the 256 MB Infinity Cache"}
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "head-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "heads": H, "head_dim": d, "prompt_len": n,
+                   "k_heavy": wl.k_heavy, "k_recent": wl.k_recent, "decode_steps": T, "layers": L,
+                   "pareto_alpha": wl.alpha, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "h2o decode_kernel (fused attention + score + evict + insert)",
+                     "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
+                     "kernel_source_digest": digest},
+        "decode_head_steps_per_s": head_steps / (sum(decode_ms) / args.steps / 1e3),
+        "prefill": {"ms_per_layer": pf_s * 1e3, "algorithmic_TFLOPs": prefill_flops / pf_s / 1e12,
+                    "mfma_frac": prefill_flops / pf_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    "note": "rowlse + colsum + select/gather + cache clear, 2 causal QK^T passes"},
+        "wall_s_timed": wall_s,
+        "single_layer": single,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

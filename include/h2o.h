@@ -1,0 +1,178 @@
+/*
+ * h2o.h -- C ABI of the MI355X (gfx950) Heavy-Hitter Oracle (H2O) KV-cache library.
+ *
+ * Citations ("H2O §x") refer to the page "H2O: Heavy-Hitter Oracle for
+ * Efficient Generative Inference of Large Language Models" (paperlayer.ai
+ * source-linked summary of arXiv 2306.14048v3), section x.
+ *
+ * The problem (H2O §2 "Problem formulation", §D "Cache eviction"): every
+ * (batch, head) pair keeps a cache of exactly k = k_heavy + k_recent slots;
+ * between two consecutive decode steps at most one cached token is evicted,
+ * chosen from normalised attention accumulated over the steps (H2O §1, §4.1,
+ * §B.2: accumulated, not averaged). Prefill reduces the prompt to heavy
+ * hitters plus recent tokens (H2O §A "Pseudocode", "System Details").
+ *
+ * Conventions shared by every call
+ *  - Device memory is owned by the caller. The library never allocates or
+ *    frees device memory; all device pointers must be 16-byte aligned and the
+ *    tensors dense and contiguous in the layouts stated below (outermost
+ *    dimension first).
+ *  - "dtype" is the element type of the K/V cache and of every query, key and
+ *    value handed in (h2o_dtype). Scores, outputs and column sums are fp32.
+ *  - Every call that takes a stream enqueues its work asynchronously on that
+ *    stream (a hipStream_t; NULL is the null stream) and returns without
+ *    waiting, except h2o_cache_state when it copies to the host. Calls on one
+ *    cache must be issued in order on one stream.
+ *  - Argument errors are detected before anything is launched: the call
+ *    returns a non-zero h2o_status, changes nothing, and h2o_last_error()
+ *    returns a message. A HIP launch error returns H2O_EDEVICE. No C++
+ *    exception crosses this interface.
+ *  - All functions are thread-safe with respect to different caches.
+ */
+#ifndef H2O_MI355X_H
+#define H2O_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* h2o_stream_t; /* a hipStream_t */
+
+typedef enum {
+  H2O_OK = 0,
+  H2O_EINVAL = 1,     /* null pointer, bad size, unsupported dtype or head dim */
+  H2O_ESTATE = 2,     /* cache not initialised, or call not allowed in its state */
+  H2O_EWORKSPACE = 3, /* prefill workspace missing or too small */
+  H2O_EDEVICE = 4     /* the HIP runtime reported an error */
+} h2o_status;
+
+typedef enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F16 = 2 } h2o_dtype;
+
+/* Limits of this build. */
+#define H2O_MAX_SLOTS 8192      /* k = k_heavy + k_recent */
+#define H2O_MAX_PROMPT 1048576  /* n */
+
+/*
+ * Cache descriptor: a plain host struct filled by h2o_cache_init. It records
+ * the shape and the caller-owned device tensors of one layer's cache:
+ *   K, V  : [batch][heads][k][head_dim] dtype, slot-indexed rows
+ *   score : [batch][heads][k] fp32, accumulated normalised attention per slot
+ *   pos   : [batch][heads][k] int32, sequence position held by the slot, -1 = empty
+ * and the host counter t_next (position of the next decode token). The number
+ * of occupied slots is always n_used = min(k, t_next), the same for all heads;
+ * slots [0, n_used) are the occupied ones.
+ * Slot layout after prefill: heavy hitters in ascending position in slots
+ * [0, k_heavy), the recent window in ascending position in [k_heavy, k) (H2O §A
+ * "System Details"); a prompt no longer than k fills slots 0..n-1 in order. A
+ * decode step writes the new token into the evicted slot, or into slot n_used
+ * while the cache is not full. Fields are read-only for the caller.
+ */
+typedef struct {
+  int32_t batch, heads, head_dim;
+  int32_t k_heavy, k_recent;
+  int32_t dtype;    /* h2o_dtype */
+  float scale;      /* softmax scale applied to q.k (1/sqrt(head_dim) usually) */
+  void* K;
+  void* V;
+  float* score;
+  int32_t* pos;
+  int32_t n_used;   /* min(k, t_next) */
+  int32_t t_next;
+  int64_t steps;    /* decode steps taken since init */
+  uint32_t magic;   /* set by h2o_cache_init */
+  uint32_t reserved;
+} h2o_cache;
+
+typedef struct {
+  int32_t n_used, t_next, k, k_heavy, k_recent;
+  int32_t reserved;
+  int64_t steps;
+} h2o_state;
+
+/*
+ * Fill *cache and clear the device state: pos = -1, score = 0 for every slot
+ * (K and V are left as they are), t_next = 0.
+ * Requires batch, heads >= 1; head_dim in {64, 128}; k_heavy >= 0;
+ * k_recent >= 1 (the recent window always holds the newest token, so a full
+ * cache always has exactly one evictable slot more than k_heavy);
+ * k <= H2O_MAX_SLOTS; scale finite and > 0; non-null device pointers.
+ */
+h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                          int32_t k_heavy, int32_t k_recent, int32_t dtype, float scale,
+                          void* K, void* V, float* score, int32_t* pos, h2o_stream_t stream);
+
+/* Bytes of device workspace h2o_prefill_select needs for a prompt of n tokens. */
+size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n);
+
+/*
+ * Prefill scoring and selection (H2O §A "Pseudocode"; attention as in H2O §D
+ * "Recursive attention").
+ *   Q, Kp, Vp : [batch][heads][n][head_dim] dtype, the prompt's queries, keys, values
+ * For every (b,h): c_j = sum over prompt rows i >= j of softmax_j'(scale*q_i.k_j')[j]
+ * (causal, own position included). If n <= k every position is kept in slots
+ * 0..n-1; otherwise the recent window n-k_recent..n-1 is kept together with
+ * the k_heavy positions in [0, n-k_recent) whose keys (c_j, j) are largest
+ * (so equal scores keep the later position). Kept slots get K/V rows copied
+ * from the prompt and score = c_j; unused slots get pos = -1, score = 0.
+ * Afterwards t_next = n.
+ *   workspace  : device buffer of at least h2o_prefill_workspace_bytes(...) bytes
+ *   colsum_out : optional [batch][heads][n] fp32 device buffer receiving c, or NULL
+ * The cache must be freshly initialised (t_next == 0). n may be 0.
+ */
+h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, const void* Vp,
+                              int32_t n, void* workspace, size_t workspace_bytes,
+                              float* colsum_out, h2o_stream_t stream);
+
+/*
+ * One decode step at position t = t_next for every (b,h) (H2O §D "Recursive
+ * attention" then "Cache eviction"; H2O §2 "Problem formulation"):
+ *   q, k_new, v_new : [batch][heads][head_dim] dtype, the new token
+ *   out             : [batch][heads][head_dim] fp32, attention output
+ *   evicted_pos     : [batch][heads] int32, evicted position or -1
+ * 1. p = softmax over the occupied slots plus the new token itself of scale*q.k.
+ * 2. out = sum p_a V_a + p_new v_new.
+ * 3. score_a += p_a for every occupied slot.
+ * 4. If the cache is full (n_used == k), the victim is the slot with the
+ *    smallest (score, pos) among slots with pos <= t - k_recent; exactly one
+ *    slot is evicted. Otherwise nothing is evicted and the slot is n_used.
+ * 5. The slot receives k_new, v_new, pos = t, score = p_new; t_next = t + 1.
+ */
+h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,
+                           float* out, int32_t* evicted_pos, h2o_stream_t stream);
+
+/*
+ * Export the cache state (checkpoint, inspection). Fills *state from the host
+ * counters. If pos_host and/or score_host are non-null ([batch][heads][k]
+ * host arrays), the device arrays are copied into them and the call waits for
+ * the stream; otherwise it does not touch the device.
+ */
+h2o_status h2o_cache_state(const h2o_cache* cache, h2o_state* state, int32_t* pos_host,
+                           float* score_host, h2o_stream_t stream);
+
+/*
+ * Restore the host counter after the caller has written K, V, score and pos
+ * back into the device tensors (resume from a checkpoint, or resynchronise
+ * from another implementation). Sets t_next and n_used = min(k, t_next).
+ */
+h2o_status h2o_cache_restore(h2o_cache* cache, int32_t t_next, int64_t steps);
+
+/*
+ * Plain decode attention over a contiguous full cache, without scores or
+ * eviction (the no-eviction comparator of the same step):
+ *   q : [batch][heads][head_dim], Kc, Vc : [batch][heads][len][head_dim] dtype
+ *   out : [batch][heads][head_dim] fp32, out = softmax(scale*q.Kc) Vc over len rows.
+ */
+h2o_status h2o_fullcache_decode(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype,
+                                float scale, int32_t len, const void* q, const void* Kc,
+                                const void* Vc, float* out, h2o_stream_t stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* h2o_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* H2O_MI355X_H */

@@ -1,0 +1,245 @@
+// C ABI of the H2O KV-cache library: validation, host-side counters, launches.
+// The entry points and their contracts are declared in include/h2o.h.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/h2o.h"
+#include "launch.h"
+
+namespace {
+
+constexpr uint32_t kMagic = 0x48324F31u;  // "H2O1"
+thread_local char g_err[512] = "";
+
+h2o_status fail(h2o_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+h2o_status device_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return H2O_OK;
+  return fail(H2O_EDEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == H2O_F32 ? 4 : 2; }
+
+h2o_status check_cache(const h2o_cache* c) {
+  if (!c) return fail(H2O_EINVAL, "cache is NULL");
+  if (c->magic != kMagic) return fail(H2O_ESTATE, "cache descriptor was not initialised by h2o_cache_init");
+  return H2O_OK;
+}
+
+size_t lse_ld(int32_t n) { return (size_t(n) + 63) & ~size_t(63); }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* h2o_last_error(void) { return g_err; }
+
+h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                          int32_t k_heavy, int32_t k_recent, int32_t dtype, float scale, void* K,
+                          void* V, float* score, int32_t* pos, h2o_stream_t stream) {
+  if (!cache) return fail(H2O_EINVAL, "cache is NULL");
+  if (batch < 1 || heads < 1) return fail(H2O_EINVAL, "batch and heads must be >= 1");
+  if (int64_t(batch) * heads > (int64_t(1) << 31) - 1) return fail(H2O_EINVAL, "batch*heads too large");
+  if (head_dim != 64 && head_dim != 128) return fail(H2O_EINVAL, "head_dim %d not supported (64, 128)", head_dim);
+  if (dtype != H2O_F32 && dtype != H2O_BF16 && dtype != H2O_F16) return fail(H2O_EINVAL, "unknown dtype %d", dtype);
+  if (k_heavy < 0) return fail(H2O_EINVAL, "k_heavy must be >= 0");
+  if (k_recent < 1) return fail(H2O_EINVAL, "k_recent must be >= 1");
+  if (int64_t(k_heavy) + k_recent > H2O_MAX_SLOTS)
+    return fail(H2O_EINVAL, "k = %lld exceeds %d slots", (long long)k_heavy + k_recent, H2O_MAX_SLOTS);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(H2O_EINVAL, "scale must be finite and > 0");
+  if (!K || !V || !score || !pos) return fail(H2O_EINVAL, "K, V, score and pos must be non-NULL");
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(score, 4) || !aligned(pos, 4))
+    return fail(H2O_EINVAL, "K and V must be 16-byte aligned, score and pos 4-byte aligned");
+
+  h2o_cache c{};
+  c.batch = batch;
+  c.heads = heads;
+  c.head_dim = head_dim;
+  c.k_heavy = k_heavy;
+  c.k_recent = k_recent;
+  c.dtype = dtype;
+  c.scale = scale;
+  c.K = K;
+  c.V = V;
+  c.score = score;
+  c.pos = pos;
+  c.n_used = 0;
+  c.t_next = 0;
+  c.steps = 0;
+  c.magic = kMagic;
+  const int64_t count = int64_t(batch) * heads * (k_heavy + k_recent);
+  h2o_status st = device_status(
+      h2o::launch_cache_clear(score, pos, count, static_cast<hipStream_t>(stream)), "h2o_cache_init");
+  if (st != H2O_OK) return st;
+  *cache = c;
+  return H2O_OK;
+}
+
+size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n) {
+  if (batch < 1 || heads < 1 || n < 0) return 0;
+  const size_t G = size_t(batch) * heads;
+  return align256(G * lse_ld(n) * sizeof(float)) + align256(G * size_t(n) * sizeof(float));
+}
+
+h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, const void* Vp,
+                              int32_t n, void* workspace, size_t workspace_bytes, float* colsum_out,
+                              h2o_stream_t stream) {
+  h2o_status st = check_cache(cache);
+  if (st != H2O_OK) return st;
+  if (cache->t_next != 0) return fail(H2O_ESTATE, "prefill needs a freshly initialised cache (t_next = %d)", cache->t_next);
+  if (n < 0 || n > H2O_MAX_PROMPT) return fail(H2O_EINVAL, "prompt length %d out of range [0, %d]", n, H2O_MAX_PROMPT);
+  if (n == 0) return H2O_OK;  // nothing to score; the cleared cache is the result
+  if (!Q || !Kp || !Vp) return fail(H2O_EINVAL, "Q, K and V must be non-NULL");
+  if (!aligned(Q, 16) || !aligned(Kp, 16) || !aligned(Vp, 16))
+    return fail(H2O_EINVAL, "Q, K and V must be 16-byte aligned");
+  const size_t need = h2o_prefill_workspace_bytes(cache->batch, cache->heads, n);
+  if (!workspace || workspace_bytes < need)
+    return fail(H2O_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (!aligned(workspace, 256)) return fail(H2O_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (colsum_out && !aligned(colsum_out, 4)) return fail(H2O_EINVAL, "colsum_out must be 4-byte aligned");
+
+  const int G = cache->batch * cache->heads;
+  h2o::PrefillArgs a{};
+  a.Q = Q;
+  a.K = Kp;
+  a.V = Vp;
+  a.lse2 = static_cast<float*>(workspace);
+  a.colsum = colsum_out ? colsum_out
+                        : reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                   align256(size_t(G) * lse_ld(n) * sizeof(float)));
+  a.cK = cache->K;
+  a.cV = cache->V;
+  a.cscore = cache->score;
+  a.cpos = cache->pos;
+  a.n = n;
+  a.k_heavy = cache->k_heavy;
+  a.k_recent = cache->k_recent;
+  a.c = cache->scale * h2o::kLog2e;
+  st = device_status(h2o::launch_prefill(cache->dtype, cache->head_dim, G, a, static_cast<hipStream_t>(stream)),
+                     "h2o_prefill_select");
+  if (st != H2O_OK) return st;
+  const int32_t k = cache->k_heavy + cache->k_recent;
+  cache->t_next = n;
+  cache->n_used = n < k ? n : k;
+  return H2O_OK;
+}
+
+h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,
+                           float* out, int32_t* evicted_pos, h2o_stream_t stream) {
+  h2o_status st = check_cache(cache);
+  if (st != H2O_OK) return st;
+  if (!q || !k_new || !v_new || !out || !evicted_pos)
+    return fail(H2O_EINVAL, "q, k_new, v_new, out and evicted_pos must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 4) || !aligned(evicted_pos, 4))
+    return fail(H2O_EINVAL, "q, k_new, v_new must be 16-byte aligned; out, evicted_pos 4-byte aligned");
+  if (cache->t_next == INT32_MAX) return fail(H2O_ESTATE, "position counter exhausted");
+
+  const int32_t k = cache->k_heavy + cache->k_recent;
+  h2o::DecodeArgs a{};
+  a.K = cache->K;
+  a.V = cache->V;
+  a.K_w = cache->K;
+  a.V_w = cache->V;
+  a.score = cache->score;
+  a.pos = cache->pos;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.out = out;
+  a.evicted = evicted_pos;
+  a.k = k;
+  a.n_used = cache->n_used;
+  a.t = cache->t_next;
+  a.k_recent = cache->k_recent;
+  a.c = cache->scale * h2o::kLog2e;
+  st = device_status(h2o::launch_decode(cache->dtype, cache->head_dim, cache->batch * cache->heads, a,
+                                        static_cast<hipStream_t>(stream)),
+                     "h2o_decode_step");
+  if (st != H2O_OK) return st;
+  cache->t_next += 1;
+  cache->n_used = cache->n_used < k ? cache->n_used + 1 : k;
+  cache->steps += 1;
+  return H2O_OK;
+}
+
+h2o_status h2o_cache_state(const h2o_cache* cache, h2o_state* state, int32_t* pos_host,
+                           float* score_host, h2o_stream_t stream) {
+  h2o_status st = check_cache(cache);
+  if (st != H2O_OK) return st;
+  if (!state) return fail(H2O_EINVAL, "state is NULL");
+  const int32_t k = cache->k_heavy + cache->k_recent;
+  const size_t count = size_t(cache->batch) * cache->heads * k;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pos_host) {
+    st = device_status(hipMemcpyAsync(pos_host, cache->pos, count * sizeof(int32_t), hipMemcpyDeviceToHost, s),
+                       "h2o_cache_state");
+    if (st != H2O_OK) return st;
+  }
+  if (score_host) {
+    st = device_status(hipMemcpyAsync(score_host, cache->score, count * sizeof(float), hipMemcpyDeviceToHost, s),
+                       "h2o_cache_state");
+    if (st != H2O_OK) return st;
+  }
+  if (pos_host || score_host) {
+    st = device_status(hipStreamSynchronize(s), "h2o_cache_state");
+    if (st != H2O_OK) return st;
+  }
+  state->n_used = cache->n_used;
+  state->t_next = cache->t_next;
+  state->k = k;
+  state->k_heavy = cache->k_heavy;
+  state->k_recent = cache->k_recent;
+  state->reserved = 0;
+  state->steps = cache->steps;
+  return H2O_OK;
+}
+
+h2o_status h2o_cache_restore(h2o_cache* cache, int32_t t_next, int64_t steps) {
+  h2o_status st = check_cache(cache);
+  if (st != H2O_OK) return st;
+  if (t_next < 0 || t_next == INT32_MAX) return fail(H2O_EINVAL, "t_next %d out of range", t_next);
+  if (steps < 0) return fail(H2O_EINVAL, "steps must be >= 0");
+  const int32_t k = cache->k_heavy + cache->k_recent;
+  cache->t_next = t_next;
+  cache->n_used = t_next < k ? t_next : k;
+  cache->steps = steps;
+  return H2O_OK;
+}
+
+h2o_status h2o_fullcache_decode(int32_t batch, int32_t heads, int32_t head_dim, int32_t dtype, float scale,
+                                int32_t len, const void* q, const void* Kc, const void* Vc, float* out,
+                                h2o_stream_t stream) {
+  if (batch < 1 || heads < 1) return fail(H2O_EINVAL, "batch and heads must be >= 1");
+  if (int64_t(batch) * heads > (int64_t(1) << 31) - 1) return fail(H2O_EINVAL, "batch*heads too large");
+  if (head_dim != 64 && head_dim != 128) return fail(H2O_EINVAL, "head_dim %d not supported (64, 128)", head_dim);
+  if (dtype != H2O_F32 && dtype != H2O_BF16 && dtype != H2O_F16) return fail(H2O_EINVAL, "unknown dtype %d", dtype);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(H2O_EINVAL, "scale must be finite and > 0");
+  if (len < 1) return fail(H2O_EINVAL, "len must be >= 1");
+  if (!q || !Kc || !Vc || !out) return fail(H2O_EINVAL, "q, K, V and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(Kc, 16) || !aligned(Vc, 16) || !aligned(out, 4))
+    return fail(H2O_EINVAL, "q, K, V must be 16-byte aligned; out 4-byte aligned");
+  h2o::DecodeArgs a{};
+  a.K = Kc;
+  a.V = Vc;
+  a.q = q;
+  a.out = out;
+  a.k = len;
+  a.n_used = len;
+  a.c = scale * h2o::kLog2e;
+  return device_status(h2o::launch_fullcache(dtype, head_dim, batch * heads, a, static_cast<hipStream_t>(stream)),
+                       "h2o_fullcache_decode");
+}
+
+}  // extern "C"

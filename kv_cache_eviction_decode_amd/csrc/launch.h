@@ -1,0 +1,60 @@
+// Internal launchers: host-side entry into each kernel family. Arguments are
+// validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h2o {
+
+// 1/ln(2): logits are kept in base-2 units so that v_exp_f32 (2^x) is the only
+// transcendental on the path.
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+  const void* K;       // [G][k][d] cache rows (or [G][len][d] full cache)
+  const void* V;
+  float* score;        // [G][k]           (scored mode only)
+  int32_t* pos;        // [G][k]           (scored mode only)
+  void* K_w;           // writable aliases of K, V for the new token (scored mode)
+  void* V_w;
+  const void* q;       // [G][d]
+  const void* k_new;   // [G][d]           (scored mode only)
+  const void* v_new;   // [G][d]           (scored mode only)
+  float* out;          // [G][d] fp32
+  int32_t* evicted;    // [G]              (scored mode only)
+  int32_t k;           // slot capacity (rows per head in K/V)
+  int32_t n_used;      // occupied slots [0, n_used), or full-cache length
+  int32_t t;           // position of the new token
+  int32_t k_recent;
+  float c;             // scale * log2(e)
+};
+
+// Fused H2O decode step: attention over n_used slots + the new token, score
+// accumulation, at most one eviction, insert. One workgroup per head.
+hipError_t launch_decode(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);
+
+// Plain attention of one query over a contiguous cache of n_used rows.
+hipError_t launch_fullcache(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);
+
+struct PrefillArgs {
+  const void* Q;   // [G][n][d]
+  const void* K;   // [G][n][d]
+  const void* V;   // [G][n][d]
+  float* lse2;     // [G][n] workspace: per-row log2-sum-exp2 of c*s
+  float* colsum;   // [G][n] column sums (workspace or caller buffer)
+  void* cK;        // cache tensors [G][k][d], [G][k]
+  void* cV;
+  float* cscore;
+  int32_t* cpos;
+  int32_t n;
+  int32_t k_heavy, k_recent;
+  float c;         // scale * log2(e)
+};
+
+hipError_t launch_prefill(int dtype, int head_dim, int G, const PrefillArgs& a, hipStream_t s);
+
+// pos = -1, score = 0 for G*k slots.
+hipError_t launch_cache_clear(float* score, int32_t* pos, int64_t count, hipStream_t s);
+
+}  // namespace h2o

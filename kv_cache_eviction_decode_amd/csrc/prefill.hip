@@ -1,0 +1,434 @@
+// H2O prefill scoring and selection for gfx950.
+//
+// Citations ("H2O §x") refer to the page "H2O: Heavy-Hitter Oracle for
+// Efficient Generative Inference of Large Language Models" (paperlayer.ai
+// summary of arXiv 2306.14048v3).
+//
+// For every (batch, head) the prompt's causal attention matrix P (row i is a
+// softmax over keys j <= i, H2O §D "Recursive attention") is reduced to its
+// column sums c_j, the accumulated attention each prompt token receives
+// (H2O §1, §4.1). c needs each row's final normaliser, so QK^T is formed
+// twice, both times on MFMA (v_mfma_f32_32x32x16_{bf16,f16}):
+//
+//   pass 1 (rowlse):  lse2_i = log2 sum_j 2^(c * s_ij), keys streamed per query
+//                     block; the tile is computed transposed (keys x queries)
+//                     so each lane owns one query column and reduces in-lane.
+//   pass 2 (colsum):  c_j = sum_i 2^(c * s_ij - lse2_i), queries streamed per key
+//                     block; each workgroup owns its key columns, so the sums
+//                     need no atomics and are deterministic.
+//
+// Then one workgroup per head selects the k_heavy largest (c_j, j) among
+// positions before the recent window with an MSB-first radix select on the
+// score bits, compacts them in ascending position order together with the
+// recent window (H2O §A "Pseudocode", "System Details") and copies the K/V
+// rows into the cache slots.
+
+#include "h2o_device.h"
+#include "launch.h"
+
+namespace h2o {
+namespace {
+
+// Blocks are dispatched round-robin over the 8 XCDs. Remap so that XCD x runs
+// a contiguous range of logical blocks (the same heads), keeping each head's
+// K and Q tiles in one XCD's L2.
+__device__ __forceinline__ int xcd_logical_block(int bid, int grid) {
+  const int per = grid >> 3;  // grid is padded to a multiple of 8
+  return (bid & 7) * per + (bid >> 3);
+}
+
+template <int DT> struct MfmaOp;
+template <> struct MfmaOp<DT_BF16> {
+  __device__ __forceinline__ static f32x16 run(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct MfmaOp<DT_F16> {
+  __device__ __forceinline__ static f32x16 run(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+// 32x32x16 MFMA operand/result layout (wave64): lane l supplies row (l % 32)
+// of A and column (l % 32) of B, each with the 8 contiguous k values
+// 8*(l/32) .. 8*(l/32)+7. Result element j (0..15) of lane l is
+// D[8*(j/4) + 4*(l/32) + j%4][l % 32].
+__device__ __forceinline__ int mfma_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+
+constexpr int kWaveCols = 64;                 // queries (pass 1) or keys (pass 2) per wave
+constexpr int kBlockCols = 4 * kWaveCols;     // per workgroup
+
+// ---------------------------------------------------------------- pass 1 (MFMA)
+template <int DT, int D>
+__global__ __launch_bounds__(256) void rowlse_mfma(PrefillArgs a, int nblk, int G, int ld_lse) {
+  constexpr int E = Elem<DT>::bytes, ROW = D * E, KS = D / 16;
+  const int L = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (L >= G * nblk) return;
+  const int head = L / nblk;
+  const int qb = nblk - 1 - L % nblk;  // longest causal extent first
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = a.n;
+  const int q0 = qb * kBlockCols + wave * kWaveCols;
+  if (q0 >= n) return;
+  const int lr = lane & 31, lh = lane >> 5;
+  const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * ROW;
+  const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * ROW;
+
+  uint4 qf[2][KS];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = min(q0 + cb * 32 + lr, n - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * ROW + (ks * 16 + lh * 8) * E);
+  }
+  const float c = a.c;
+  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+  const int qlast = min(q0 + kWaveCols, n) - 1;
+  const int ntiles = qlast / 32 + 1;
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int key0 = kt * 32;
+    const int kr = min(key0 + lr, n - 1);
+    uint4 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(Kh + size_t(kr) * ROW + (ks * 16 + lh * 8) * E);
+    f32x16 acc[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      acc[cb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc[cb] = MfmaOp<DT>::run(kf[ks], qf[cb][ks], acc[cb]);
+    }
+    // acc[cb][j] = s(query q0 + 32cb + lr, key key0 + mfma_row(j))
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int qi = q0 + cb * 32 + lr;
+      const bool diag = key0 + 31 > q0 + cb * 32;
+      float s[16];
+      float tm = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        s[j] = (diag && key0 + mfma_row(j, lane) > qi) ? kNegInf : acc[cb][j];
+        tm = fmaxf(tm, s[j]);
+      }
+      const float mn = fmaxf(m[cb], tm);
+      if (mn != kNegInf) {
+        const float mnc = mn * c;
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) t += fast_exp2(fmaf(s[j], c, -mnc));
+        l[cb] = fmaf(l[cb], fast_exp2((m[cb] - mn) * c), t);
+        m[cb] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float mo = __shfl_xor(m[cb], 32);
+    const float lo = __shfl_xor(l[cb], 32);
+    const float M = fmaxf(m[cb], mo);
+    const float Lsum = l[cb] * fast_exp2((m[cb] - M) * c) + lo * fast_exp2((mo - M) * c);
+    const int qi = q0 + cb * 32 + lr;
+    if (lh == 0 && qi < n) a.lse2[size_t(head) * ld_lse + qi] = M * c + fast_log2(Lsum);
+  }
+}
+
+// ---------------------------------------------------------------- pass 2 (MFMA)
+template <int DT, int D>
+__global__ __launch_bounds__(256) void colsum_mfma(PrefillArgs a, int nblk, int G, int ld_lse) {
+  constexpr int E = Elem<DT>::bytes, ROW = D * E, KS = D / 16;
+  const int L = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (L >= G * nblk) return;
+  const int head = L / nblk;
+  const int kb = L % nblk;  // smallest key block = most query tiles, first
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = a.n;
+  const int k0 = kb * kBlockCols + wave * kWaveCols;
+  if (k0 >= n) return;
+  const int lr = lane & 31, lh = lane >> 5;
+  const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * ROW;
+  const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * ROW;
+  const float* lse = a.lse2 + size_t(head) * ld_lse;
+
+  uint4 kf[2][KS];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = min(k0 + cb * 32 + lr, n - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[cb][ks] = ld16(Kh + size_t(r) * ROW + (ks * 16 + lh * 8) * E);
+  }
+  const float c = a.c;
+  float sum[2] = {0.f, 0.f}, comp[2] = {0.f, 0.f};
+  const int nqt = (n + 31) / 32;
+  for (int qt = k0 / 32; qt < nqt; ++qt) {
+    const int qrow0 = qt * 32;
+    const int qr = min(qrow0 + lr, n - 1);
+    uint4 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(Qh + size_t(qr) * ROW + (ks * 16 + lh * 8) * E);
+    float lq[16];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float4 v = *reinterpret_cast<const float4*>(lse + qrow0 + 8 * jj + 4 * lh);
+      lq[4 * jj] = v.x;
+      lq[4 * jj + 1] = v.y;
+      lq[4 * jj + 2] = v.z;
+      lq[4 * jj + 3] = v.w;
+    }
+    f32x16 acc[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      acc[cb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc[cb] = MfmaOp<DT>::run(qf[ks], kf[cb][ks], acc[cb]);
+    }
+    // acc[cb][j] = s(query qrow0 + mfma_row(j), key k0 + 32cb + lr)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int kj = k0 + cb * 32 + lr;
+      const bool edge = (qrow0 < k0 + cb * 32 + 31) || (qrow0 + 31 >= n);
+      float t = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int qi = qrow0 + mfma_row(j, lane);
+        const float x = fast_exp2(fmaf(acc[cb][j], c, -lq[j]));
+        t += (edge && (qi < kj || qi >= n)) ? 0.f : x;
+      }
+      // compensated accumulation across query tiles
+      const float y = t - comp[cb];
+      const float s2 = sum[cb] + y;
+      comp[cb] = (s2 - sum[cb]) - y;
+      sum[cb] = s2;
+    }
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float mine = sum[cb] - comp[cb];
+    const float other = __shfl_xor(mine, 32);
+    const int kj = k0 + cb * 32 + lr;
+    if (lh == 0 && kj < n) a.colsum[size_t(head) * n + kj] = mine + other;
+  }
+}
+
+// ---------------------------------------------------------------- fp32 (VALU)
+// fp32 inputs have no dense MFMA rate worth using at these sizes; one thread
+// per query (pass 1) or per key (pass 2).
+template <int D>
+__global__ __launch_bounds__(256) void rowlse_valu(PrefillArgs a, int nblk, int ld_lse) {
+  const int head = blockIdx.x / nblk;
+  const int i = (blockIdx.x % nblk) * 256 + threadIdx.x;
+  const int n = a.n;
+  if (i >= n) return;
+  const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
+  const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
+  const float c = a.c;
+  float m = kNegInf, l = 0.f;
+  for (int j = 0; j <= i; ++j) {
+    float s = 0.f;
+    for (int e = 0; e < D; ++e) s = fmaf(Q[size_t(i) * D + e], K[size_t(j) * D + e], s);
+    const float mn = fmaxf(m, s);
+    l = fmaf(l, fast_exp2((m - mn) * c), fast_exp2((s - mn) * c));
+    m = mn;
+  }
+  a.lse2[size_t(head) * ld_lse + i] = m * c + fast_log2(l);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void colsum_valu(PrefillArgs a, int nblk, int ld_lse) {
+  const int head = blockIdx.x / nblk;
+  const int j = (blockIdx.x % nblk) * 256 + threadIdx.x;
+  const int n = a.n;
+  if (j >= n) return;
+  const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
+  const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
+  const float* lse = a.lse2 + size_t(head) * ld_lse;
+  const float c = a.c;
+  float sum = 0.f, comp = 0.f;
+  for (int i = j; i < n; ++i) {
+    float s = 0.f;
+    for (int e = 0; e < D; ++e) s = fmaf(Q[size_t(i) * D + e], K[size_t(j) * D + e], s);
+    const float y = fast_exp2(fmaf(s, c, -lse[i])) - comp;
+    const float t = sum + y;
+    comp = (t - sum) - y;
+    sum = t;
+  }
+  a.colsum[size_t(head) * n + j] = sum - comp;
+}
+
+// ---------------------------------------------------------------- select + gather
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+
+__device__ int block_exclusive_scan(int v, int* sm_wave, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sm_wave[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int t = sm_wave[w];
+    before += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return before + x - v;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
+  constexpr int E = Elem<DT>::bytes, ROW = D * E, LPR = ROW / 16;
+  __shared__ int slot_pos[8192];
+  __shared__ int hist[256];
+  __shared__ int sm_wave[kSelWaves];
+  __shared__ int sm_digit, sm_above, sm_P;
+
+  const int head = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = a.n, kh = a.k_heavy, kr = a.k_recent, k = kh + kr;
+  const float* col = a.colsum + size_t(head) * n;
+
+  if (n <= k) {
+    for (int s = tid; s < k; s += kSelThreads) slot_pos[s] = s < n ? s : -1;
+  } else {
+    const int C = n - kr;  // heavy-hitter candidates: positions [0, C)
+    uint32_t T = 0;
+    int P = C;
+    if (kh > 0) {
+      uint32_t prefix = 0, pmask = 0;
+      int need = kh;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+        for (int j = tid; j < C; j += kSelThreads) {
+          const uint32_t b = __float_as_uint(col[j]);
+          if ((b & pmask) == prefix) atomicAdd(&hist[(b >> shift) & 255], 1);
+        }
+        __syncthreads();
+        // digit d scanned from the top: v = hist[255 - tid]
+        const int v = tid < 256 ? hist[255 - tid] : 0;
+        int tot;
+        const int above = block_exclusive_scan(v, sm_wave, tot);
+        if (tid < 256 && above < need && above + v >= need) {
+          sm_digit = 255 - tid;
+          sm_above = above;
+        }
+        __syncthreads();
+        need -= sm_above;
+        prefix |= uint32_t(sm_digit) << shift;
+        pmask |= 255u << shift;
+        __syncthreads();
+      }
+      T = prefix;
+      // Ties at T: keep the `need` of them with the largest positions.
+      int taken = 0;
+      for (int base = ((C - 1) / kSelThreads) * kSelThreads; base >= 0; base -= kSelThreads) {
+        const int j = base + tid;
+        const int tie = (j < C && __float_as_uint(col[j]) == T) ? 1 : 0;
+        int tot;
+        const int below = block_exclusive_scan(tie, sm_wave, tot);
+        const int above = tot - below - tie;  // ties in this chunk after j
+        if (tie && taken + above == need - 1) sm_P = j;
+        __syncthreads();
+        if (taken + tot >= need) break;
+        taken += tot;
+      }
+      P = sm_P;
+    }
+    // Compact the selected candidates in ascending position order.
+    int base_slot = 0;
+    for (int base = 0; base < C; base += kSelThreads) {
+      const int j = base + tid;
+      int sel = 0;
+      if (kh > 0 && j < C) {
+        const uint32_t b = __float_as_uint(col[j]);
+        sel = (b > T || (b == T && j >= P)) ? 1 : 0;
+      }
+      int tot;
+      const int off = block_exclusive_scan(sel, sm_wave, tot);
+      if (sel && base_slot + off < kh) slot_pos[base_slot + off] = j;
+      base_slot += tot;
+    }
+    for (int s = tid; s < kr; s += kSelThreads) slot_pos[kh + s] = n - kr + s;
+  }
+  __syncthreads();
+
+  const size_t hk = size_t(head) * k;
+  for (int s = tid; s < k; s += kSelThreads) {
+    const int p = slot_pos[s];
+    a.cpos[hk + s] = p;
+    a.cscore[hk + s] = p >= 0 ? col[p] : 0.f;
+  }
+  const int filled = min(n, k);
+  const int sub = tid % LPR;
+  const char* Kp = static_cast<const char*>(a.K) + size_t(head) * n * ROW + sub * 16;
+  const char* Vp = static_cast<const char*>(a.V) + size_t(head) * n * ROW + sub * 16;
+  char* cK = static_cast<char*>(a.cK) + hk * ROW + sub * 16;
+  char* cV = static_cast<char*>(a.cV) + hk * ROW + sub * 16;
+  for (int s = tid / LPR; s < filled; s += kSelThreads / LPR) {
+    const int p = slot_pos[s];
+    if (p < 0 || p >= n) continue;  // cannot happen for a consistent selection
+    const size_t src = size_t(p) * ROW;
+    st16(cK + size_t(s) * ROW, ld16(Kp + src));
+    st16(cV + size_t(s) * ROW, ld16(Vp + src));
+  }
+}
+
+__global__ void cache_clear(float* score, int32_t* pos, int64_t count) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < count;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    score[i] = 0.f;
+    pos[i] = -1;
+  }
+}
+
+int pad8(int x) { return (x + 7) & ~7; }
+
+template <int DT, int D>
+hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
+  const int ld_lse = (a.n + 63) & ~63;
+  if constexpr (DT == DT_F32) {
+    const int nblk = (a.n + 255) / 256;
+    hipLaunchKernelGGL((rowlse_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
+    hipLaunchKernelGGL((colsum_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
+  } else {
+    const int nblk = (a.n + kBlockCols - 1) / kBlockCols;
+    const int grid = pad8(G * nblk);
+    hipLaunchKernelGGL((rowlse_mfma<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
+    hipLaunchKernelGGL((colsum_mfma<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
+  }
+  hipLaunchKernelGGL((select_gather<DT, D>), dim3(G), dim3(kSelThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(int dtype, int head_dim, int G, const PrefillArgs& a, hipStream_t s) {
+  if (G <= 0 || a.n <= 0) return hipSuccess;
+  switch (dtype * 1000 + head_dim) {
+    case DT_F32 * 1000 + 64: return prefill_typed<DT_F32, 64>(G, a, s);
+    case DT_F32 * 1000 + 128: return prefill_typed<DT_F32, 128>(G, a, s);
+    case DT_BF16 * 1000 + 64: return prefill_typed<DT_BF16, 64>(G, a, s);
+    case DT_BF16 * 1000 + 128: return prefill_typed<DT_BF16, 128>(G, a, s);
+    case DT_F16 * 1000 + 64: return prefill_typed<DT_F16, 64>(G, a, s);
+    case DT_F16 * 1000 + 128: return prefill_typed<DT_F16, 128>(G, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_cache_clear(float* score, int32_t* pos, int64_t count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(cache_clear, dim3(unsigned(blocks)), dim3(256), 0, s, score, pos, count);
+  return hipGetLastError();
+}
+
+}  // namespace h2o

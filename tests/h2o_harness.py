@@ -1,0 +1,222 @@
+"""Step-by-step parity of the HIP path against the fp64 oracle (test helper).
+
+Both sides consume the same seeded, dtype-rounded inputs from ``workload``.
+The GPU runs every head; the oracle follows a sample of heads (all heads for
+small cases). After prefill and after every decode step the GPU's state for
+the sampled heads is compared with the oracle's and then resynchronised from
+it: scores always (fp64 -> fp32), and pos/K/V for heads whose selection or
+eviction legitimately differed (oracle margin below 1e-5 relative, where
+either choice is correct).
+
+Tolerances: attention outputs within max-abs 2e-2 for 16-bit K/V and 1e-4
+for fp32; scores within 1e-4 relative; selected and evicted positions
+bit-exact unless the oracle margin is below 1e-5 relative, in which case the
+GPU's choice must be one of the near-tied correct ones.
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from kv_cache_eviction_decode_amd import H2OCache
+from oracle import H2OOracle
+from workload import Workload, make_decode, make_prompt
+
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+MARGIN = 1e-5
+SCORE_RTOL = 1e-4
+SCORE_ATOL = 1e-7
+
+
+def out_tolerance(dtype: str) -> float:
+    return 1e-4 if dtype == "f32" else 2e-2
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """float32 array holding dtype-exact values -> device tensor of that dtype (exact)."""
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device).to(TORCH_DTYPE[dtype])
+
+
+@dataclass
+class Report:
+    steps: int = 0
+    max_out_err: float = 0.0
+    max_score_rel: float = 0.0
+    max_colsum_rel: float = 0.0
+    excused_selections: int = 0
+    excused_evictions: int = 0
+    evictions_checked: int = 0
+    notes: list = field(default_factory=list)
+
+
+def _rel_err(got, ref):
+    return np.abs(got - ref) / np.maximum(np.abs(ref), SCORE_ATOL / SCORE_RTOL)
+
+
+class ParityRun:
+    def __init__(self, wl: Workload, steps: int, sample=None, device="cuda", seed=None):
+        self.wl = wl
+        self.steps = steps
+        self.device = torch.device(device)
+        G = wl.n_heads_total
+        self.sample = np.arange(G) if sample is None else np.asarray(sample)
+        self.sample_t = torch.from_numpy(self.sample).to(self.device)
+        B, H, n, d = wl.batch, wl.heads, wl.prompt_len, wl.head_dim
+        log(f"[parity] {wl.describe()} steps={steps} sampled_heads={self.sample.size}")
+        Q, K, V = make_prompt(wl, seed=seed)
+        qd, kd, vd = make_decode(wl, steps=steps, seed=seed)
+        self.oQ, self.oK, self.oV = Q[self.sample], K[self.sample], V[self.sample]
+        self.oq, self.ok, self.ov = qd[self.sample], kd[self.sample], vd[self.sample]
+        dev = self.device
+        self.Q = to_device(Q, wl.dtype, dev).view(B, H, n, d)
+        self.K = to_device(K, wl.dtype, dev).view(B, H, n, d)
+        self.V = to_device(V, wl.dtype, dev).view(B, H, n, d)
+        del Q, K, V
+        # decode inputs staged as [T, B, H, d]
+        self.q = to_device(qd.transpose(1, 0, 2), wl.dtype, dev).view(steps, B, H, d)
+        self.k = to_device(kd.transpose(1, 0, 2), wl.dtype, dev).view(steps, B, H, d)
+        self.v = to_device(vd.transpose(1, 0, 2), wl.dtype, dev).view(steps, B, H, d)
+        del qd, kd, vd
+        self.cache = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, TORCH_DTYPE[wl.dtype], wl.scale, dev)
+        self.orc = H2OOracle(self.sample.size, d, wl.k_heavy, wl.k_recent, wl.scale)
+        self.report = Report()
+
+    # -- views of the sampled heads on the GPU
+    def _gpu_sampled(self, t: torch.Tensor) -> np.ndarray:
+        flat = t.reshape(self.wl.n_heads_total, *t.shape[2:])
+        return flat.index_select(0, self.sample_t).float().cpu().numpy() if t.is_floating_point() \
+            else flat.index_select(0, self.sample_t).cpu().numpy()
+
+    def _write_sampled(self, t: torch.Tensor, values: np.ndarray, heads=None):
+        flat = t.view(self.wl.n_heads_total, *t.shape[2:])
+        idx = self.sample if heads is None else self.sample[heads]
+        src = values if heads is None else values[heads]
+        flat[torch.from_numpy(idx).to(self.device)] = torch.from_numpy(np.ascontiguousarray(src)).to(
+            self.device).to(t.dtype)
+
+    def resync(self, heads_full=()):
+        """GPU state of the sampled heads <- oracle state."""
+        self._write_sampled(self.cache.score, self.orc.score.astype(np.float32))
+        heads_full = np.asarray(sorted(set(int(h) for h in heads_full)), dtype=np.int64)
+        if heads_full.size:
+            self._write_sampled(self.cache.pos, self.orc.pos.astype(np.int32), heads_full)
+            self._write_sampled(self.cache.K, self.orc.K.astype(np.float32), heads_full)
+            self._write_sampled(self.cache.V, self.orc.V.astype(np.float32), heads_full)
+
+    # -- prefill
+    def prefill(self, check_rows=True):
+        wl, rep = self.wl, self.report
+        n = wl.prompt_len
+        colsum = torch.empty(wl.batch, wl.heads, n, dtype=torch.float32, device=self.device) if n else None
+        self.cache.prefill_select(self.Q, self.K, self.V, colsum_out=colsum)
+        pre = self.orc.prefill(self.oQ, self.oK, self.oV)
+        torch.cuda.synchronize()
+        assert self.cache.n_used == self.orc.n_used and self.cache.t_next == self.orc.t == n
+        gpos = self._gpu_sampled(self.cache.pos)
+        gscore = self._gpu_sampled(self.cache.score)
+        differ = []
+        if n:
+            gcol = self._gpu_sampled(colsum)
+            rel = _rel_err(gcol, pre.colsum)
+            rep.max_colsum_rel = float(rel.max())
+            assert rel.max() <= SCORE_RTOL, f"colsum rel err {rel.max():.3g}"
+        for g in range(self.sample.size):
+            if np.array_equal(gpos[g], self.orc.pos[g]):
+                continue
+            # near-tie at the selection boundary: either set is correct
+            assert pre.margin[g] < MARGIN, f"head {self.sample[g]}: selection differs, margin {pre.margin[g]:.3g}"
+            self._check_valid_selection(gpos[g], pre.colsum[g])
+            rep.excused_selections += 1
+            differ.append(g)
+        same = np.array([g not in differ for g in range(self.sample.size)])
+        if same.any():
+            np.testing.assert_array_less(_rel_err(gscore[same], self.orc.score[same]), SCORE_RTOL * (1 + 1e-9))
+        if check_rows and n:
+            self._check_rows(gpos)
+        self.resync(differ)
+
+    def _check_valid_selection(self, pos, colsum):
+        wl = self.wl
+        n, kh, kr = wl.prompt_len, wl.k_heavy, wl.k_recent
+        heavy, recent = pos[:kh], pos[kh:]
+        assert recent.tolist() == list(range(n - kr, n))
+        assert np.all(np.diff(heavy) > 0) and heavy.max() < n - kr
+        cand = np.ones(n - kr, bool)
+        cand[heavy] = False
+        lo_kept = colsum[heavy].min()
+        hi_dropped = colsum[: n - kr][cand].max()
+        assert lo_kept >= hi_dropped * (1 - MARGIN), "GPU selection is not a near-tie alternative"
+
+    def _check_rows(self, gpos):
+        """Cache rows must be bit-exact copies of the prompt rows they hold."""
+        flatK = self.cache.K.view(self.wl.n_heads_total, self.wl.k, -1)
+        flatV = self.cache.V.view(self.wl.n_heads_total, self.wl.k, -1)
+        pK = self.K.view(self.wl.n_heads_total, self.wl.prompt_len, -1)
+        pV = self.V.view(self.wl.n_heads_total, self.wl.prompt_len, -1)
+        for g, h in enumerate(self.sample[:16]):
+            live = np.nonzero(gpos[g] >= 0)[0]
+            src = torch.from_numpy(gpos[g][live].astype(np.int64)).to(self.device)
+            dst = torch.from_numpy(live.astype(np.int64)).to(self.device)
+            assert torch.equal(flatK[h].index_select(0, dst), pK[h].index_select(0, src))
+            assert torch.equal(flatV[h].index_select(0, dst), pV[h].index_select(0, src))
+
+    # -- decode
+    def decode(self, steps=None):
+        wl, rep = self.wl, self.report
+        steps = self.steps if steps is None else steps
+        tol = out_tolerance(wl.dtype)
+        out = torch.empty(wl.batch, wl.heads, wl.head_dim, dtype=torch.float32, device=self.device)
+        ev = torch.empty(wl.batch, wl.heads, dtype=torch.int32, device=self.device)
+        for t in range(steps):
+            pos_before = self.orc.pos.copy()
+            score_before = self.orc.score.copy()
+            tpos = self.orc.t
+            self.cache.decode_step(self.q[t], self.k[t], self.v[t], out, ev)
+            st = self.orc.decode_step(self.oq[:, t], self.ok[:, t], self.ov[:, t])
+            gout = self._gpu_sampled(out)
+            gev = self._gpu_sampled(ev)
+            gscore = self._gpu_sampled(self.cache.score)
+            gpos = self._gpu_sampled(self.cache.pos)
+            err = float(np.abs(gout - st.out).max()) if gout.size else 0.0
+            rep.max_out_err = max(rep.max_out_err, err)
+            assert err <= tol, f"step {t}: out max abs err {err:.3g} > {tol}"
+            differ = []
+            for g in range(self.sample.size):
+                rep.evictions_checked += int(st.evicted[g] >= 0)
+                if gev[g] == st.evicted[g]:
+                    continue
+                assert st.margin[g] < MARGIN, (
+                    f"step {t} head {self.sample[g]}: evicted {gev[g]} vs oracle {st.evicted[g]}, "
+                    f"margin {st.margin[g]:.3g}")
+                self._check_valid_eviction(g, gev[g], pos_before[g], score_before[g], st, tpos)
+                rep.excused_evictions += 1
+                differ.append(g)
+            same = np.array([g not in differ for g in range(self.sample.size)])
+            if same.any():
+                assert np.array_equal(gpos[same], self.orc.pos[same]), f"step {t}: pos differs"
+                rel = _rel_err(gscore[same], self.orc.score[same])
+                rep.max_score_rel = max(rep.max_score_rel, float(rel.max()))
+                assert rel.max() <= SCORE_RTOL, f"step {t}: score rel err {rel.max():.3g}"
+            self.resync(differ)
+            rep.steps += 1
+        return rep
+
+    def _check_valid_eviction(self, g, gpu_evicted, pos_before, score_before, st, tpos):
+        """The GPU's victim must be eligible and tie (within MARGIN) with the oracle's."""
+        k = pos_before.size
+        acc = score_before + st.probs[g][:k]  # accumulated scores before the insert
+        mask = pos_before == gpu_evicted
+        assert mask.sum() == 1, "GPU evicted a position that was not cached"
+        assert gpu_evicted <= tpos - self.wl.k_recent, "GPU evicted a token inside the recent window"
+        elig = pos_before <= tpos - self.wl.k_recent
+        smallest = acc[elig].min()
+        assert acc[mask][0] <= smallest * (1 + MARGIN), \
+            f"GPU victim score {acc[mask][0]} not within margin of {smallest}"

@@ -1,0 +1,186 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases run the oracle on every head; they span several prefill tiles,
+ragged tails, empty and tiny prompts, prompts shorter than the cache,
+k_heavy = 0, the largest k, every dtype and both head sizes. The named
+workloads run at their full shapes (same grid as the benchmark) with the
+oracle following a seeded sample of heads.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from h2o_harness import TORCH_DTYPE, ParityRun, log, out_tolerance, to_device
+from workload import WORKLOADS, Workload, make_decode, make_prompt, sample_heads
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # name, B, H, d, dtype, n, k_heavy, k_recent, T, alpha, sink
+    ("ragged_bf16_d128", 2, 3, 128, "bf16", 300, 20, 20, 60, 1.5, 0.0),
+    ("ragged_f16_d64", 1, 5, 64, "f16", 517, 33, 34, 40, 1.5, 0.0),
+    ("fills_bf16_d64", 1, 3, 64, "bf16", 20, 24, 24, 50, 1.5, 0.0),
+    ("local_only_f32_d128", 1, 2, 128, "f32", 129, 0, 33, 30, 1.5, 0.0),
+    ("empty_prompt_bf16", 1, 2, 128, "bf16", 0, 8, 8, 40, 1.5, 0.0),
+    ("one_token_bf16", 2, 1, 128, "bf16", 1, 1, 1, 20, 1.5, 0.0),
+    ("n_eq_k_plus_1_f16", 1, 2, 128, "f16", 65, 32, 32, 10, 1.5, 0.0),
+    ("sink_f16_d128", 1, 2, 128, "f16", 2048, 205, 205, 16, 1.5, 4.0),
+    ("f32_d64_odd_k", 2, 2, 64, "f32", 200, 7, 6, 30, 1.2, 0.0),
+    ("bf16_long_tail", 1, 1, 128, "bf16", 1500, 100, 1, 24, 1.2, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(gpu, case):
+    name, B, H, d, dt, n, kh, kr, T, alpha, sink = case
+    wl = Workload(name, B, H, d, dt, n, kh, kr, T, alpha, sink, seed=zlib.crc32(name.encode()) % 10000)
+    run = ParityRun(wl, T)
+    run.prefill()
+    rep = run.decode()
+    log(f"[parity] {name}: {rep}")
+    assert rep.steps == T
+
+
+def test_tiny_f32_workload_full(gpu):
+    wl = WORKLOADS["tiny_f32"]
+    run = ParityRun(wl, wl.steps)
+    run.prefill()
+    rep = run.decode()
+    log(f"[parity] tiny_f32: {rep}")
+    assert rep.evictions_checked == wl.n_heads_total * wl.steps
+
+
+def test_max_slots(gpu):
+    wl = Workload("max_slots", 1, 1, 128, "bf16", 8300, 4096, 4096, 6, 1.5, 0.0, 31)
+    run = ParityRun(wl, wl.steps)
+    run.prefill()
+    rep = run.decode()
+    log(f"[parity] max_slots: {rep}")
+
+
+FULL = [("opt6.7b_layer", 512, 32), ("opt30b_layer", 64, 16),
+        ("long_context", 24, 4), ("large_batch_f16", 48, 16)]
+
+
+@pytest.mark.parametrize("name,steps,nsample", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled_parity(gpu, name, steps, nsample):
+    wl = WORKLOADS[name]
+    run = ParityRun(wl, steps, sample=sample_heads(wl, nsample))
+    run.prefill()
+    rep = run.decode()
+    log(f"[parity] {name} full size: {rep}")
+    assert rep.steps == steps
+
+
+def test_uniform_attention_closed_form_full_shape(gpu):
+    """All-zero queries at the OPT-6.7B layer shape: column sums are harmonic
+    differences, selection is first k_heavy + window, every step evicts
+    t - k_recent and outputs are plain means of the cached values."""
+    wl = WORKLOADS["opt6.7b_layer"]
+    B, H, d, n, kh, kr = wl.batch, wl.heads, wl.head_dim, wl.prompt_len, wl.k_heavy, wl.k_recent
+    T = 24
+    dev = torch.device("cuda")
+    _, K, V = make_prompt(wl)
+    _, kd, vd = make_decode(wl, steps=T)
+    from kv_cache_eviction_decode_amd import H2OCache
+    cache = H2OCache(B, H, d, kh, kr, torch.bfloat16, wl.scale, dev)
+    Qz = torch.zeros(B, H, n, d, dtype=torch.bfloat16, device=dev)
+    Kg = to_device(K, "bf16", dev).view(B, H, n, d)
+    Vg = to_device(V, "bf16", dev).view(B, H, n, d)
+    colsum = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    cache.prefill_select(Qz, Kg, Vg, colsum_out=colsum)
+    Hn = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    np.testing.assert_allclose(colsum.cpu().numpy().reshape(-1, n), np.broadcast_to(Hn[n] - Hn[:n], (B * H, n)),
+                               rtol=1e-4)
+    expect = np.array(list(range(kh)) + list(range(n - kr, n)), dtype=np.int32)
+    assert (cache.pos.cpu().numpy().reshape(-1, wl.k) == expect).all()
+    allv = np.concatenate([V, vd], axis=1)  # [G, n+T, d] float64-exact values
+    members = np.broadcast_to(expect, (B * H, wl.k)).copy()
+    qz = torch.zeros(B, H, d, dtype=torch.bfloat16, device=dev)
+    kdg = to_device(kd.transpose(1, 0, 2), "bf16", dev).view(T, B, H, d)
+    vdg = to_device(vd.transpose(1, 0, 2), "bf16", dev).view(T, B, H, d)
+    for t in range(T):
+        out, ev = cache.decode_step(qz, kdg[t], vdg[t])
+        pos_t = n + t
+        assert (ev.cpu().numpy() == pos_t - kr).all(), f"step {t}"
+        idx = np.concatenate([members, np.full((B * H, 1), pos_t)], axis=1)
+        mean = np.take_along_axis(allv, idx[:, :, None], axis=1).mean(axis=1)
+        err = np.abs(out.cpu().numpy().reshape(B * H, d) - mean).max()
+        assert err <= 1e-5, f"step {t}: {err}"
+        members[members == pos_t - kr] = pos_t
+
+
+def test_deterministic_and_resumable(gpu):
+    """Two runs are bit-identical; snapshot + restore into a fresh cache and
+    continue gives the same bits as the uninterrupted run."""
+    from kv_cache_eviction_decode_amd import H2OCache
+    wl = Workload("det", 4, 8, 128, "bf16", 700, 64, 64, 40, 1.5, 0.0, 5)
+    B, H, d, n = wl.batch, wl.heads, wl.head_dim, wl.prompt_len
+    dev = torch.device("cuda")
+    Q, K, V = (to_device(x, "bf16", dev).view(B, H, n, d) for x in make_prompt(wl))
+    qd, kd, vd = (to_device(x.transpose(1, 0, 2), "bf16", dev).view(wl.steps, B, H, d) for x in make_decode(wl))
+
+    def run(split=None):
+        c = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, torch.bfloat16, wl.scale, dev)
+        c.prefill_select(Q, K, V)
+        outs, evs = [], []
+        for t in range(wl.steps):
+            if split is not None and t == split:
+                st, pos_h, score_h = c.state(copy=True)
+                K_snap, V_snap = c.K.clone(), c.V.clone()
+                c = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, torch.bfloat16, wl.scale, dev)
+                c.K.copy_(K_snap)
+                c.V.copy_(V_snap)
+                c.pos.copy_(pos_h.to(dev))
+                c.score.copy_(score_h.to(dev))
+                c.restore(st.t_next, st.steps)
+            o, e = c.decode_step(qd[t], kd[t], vd[t])
+            outs.append(o.clone())
+            evs.append(e.clone())
+        return torch.stack(outs), torch.stack(evs), c.score.clone(), c.pos.clone(), c.K.clone()
+
+    a = run()
+    b = run()
+    c = run(split=wl.steps // 2)
+    for x, y, z in zip(a, b, c):
+        assert torch.equal(x, y)
+        assert torch.equal(x, z)
+
+
+def test_fullcache_comparator_matches_oracle(gpu):
+    from oracle import H2OOracle
+    from kv_cache_eviction_decode_amd import h2o_fullcache_decode
+    wl = Workload("full", 2, 4, 128, "f16", 333, 0, 1, 1, 1.5, 0.0, 8)
+    B, H, d, L = wl.batch, wl.heads, wl.head_dim, wl.prompt_len
+    dev = torch.device("cuda")
+    Q, K, V = make_prompt(wl)
+    q, _, _ = make_decode(wl, steps=1)
+    out = torch.empty(B, H, d, dtype=torch.float32, device=dev)
+    h2o_fullcache_decode(to_device(q[:, 0], "f16", dev).view(B, H, d), to_device(K, "f16", dev).view(B, H, L, d),
+                         to_device(V, "f16", dev).view(B, H, L, d), out, wl.scale)
+    # oracle: a never-full cache holding the first L-1 tokens; token L-1 arrives as the new one
+    orc = H2OOracle(B * H, d, L, 1, wl.scale)
+    orc.prefill(Q[:, :L - 1], K[:, :L - 1], V[:, :L - 1])
+    st = orc.decode_step(q[:, 0], K[:, L - 1], V[:, L - 1])
+    err = np.abs(out.cpu().numpy().reshape(B * H, d) - st.out).max()
+    assert err <= out_tolerance("f16"), err
+
+
+def test_state_errors_on_gpu(gpu):
+    from kv_cache_eviction_decode_amd import H2OCache, H2OError, binding
+    dev = torch.device("cuda")
+    c = H2OCache(1, 2, 64, 4, 4, torch.bfloat16, None, dev)
+    Q = torch.zeros(1, 2, 10, 64, dtype=torch.bfloat16, device=dev)
+    small = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(H2OError, match="EWORKSPACE"):
+        binding.h2o_prefill_select(c.desc, Q, Q, Q, small, None, None, c.device)
+    c.prefill_select(Q, Q, Q)
+    with pytest.raises(H2OError, match="ESTATE"):
+        c.prefill_select(Q, Q, Q)
+    with pytest.raises(ValueError):
+        c.decode_step(torch.zeros(1, 2, 128, dtype=torch.bfloat16, device=dev), Q[:, :, 0], Q[:, :, 0])
+    st = c.state()
+    assert (st.n_used, st.t_next, st.k) == (8, 10, 8)
+    torch.cuda.synchronize()
