@@ -4,24 +4,29 @@
 // Efficient Generative Inference of Large Language Models" (paperlayer.ai
 // summary of arXiv 2306.14048v3).
 //
-// One workgroup (4 waves) per (batch, head). The step is a matrix-vector
-// product over k cached rows, so it is HBM-bound and uses VALU dot products,
-// not MFMA. Rows are streamed with 16-byte loads: a row of d elements is read
-// by LPR = d*bytes/16 consecutive lanes, so one wave-wide load covers RPU =
+// The step is a matrix-vector product over the k cached rows of every
+// (batch, head), so it is HBM-bound and uses VALU dot products, not MFMA.
+// Rows are streamed with 16-byte loads: a row of d elements is read by
+// LPR = d*bytes/16 consecutive lanes, so one wave-wide load covers RPU =
 // 64/LPR consecutive rows (1 KiB, fully coalesced). Each lane group keeps its
-// own online-softmax partial (running max m, sum l, and its slice of the
-// P.V accumulator) over the rows it streamed, so K and V loads of a batch are
-// issued together and no cross-lane traffic is needed inside the loop except
-// the DPP reduction of each row's dot product. Raw logits (base-2 units) are
-// parked in LDS; after the partials are merged, the exact probability of every
-// slot is known and the accumulated scores are updated (H2O §1 "Greedy
-// algorithm for low-cost policy", §B.2: accumulated, not averaged).
-//
-// The victim is the slot with the smallest (score, pos) key among slots
-// outside the recent window (H2O §2 "Problem formulation": one eviction at
-// most; §D "Cache eviction"), found with a wave shuffle min and an LDS merge.
-// The new token then takes the victim's slot (or slot n_used while the cache
+// own online-softmax partial (running max m, sum l and its slice of the P.V
+// accumulator) over the rows it streamed, so K and V loads are issued
+// together and the only cross-lane work inside the loop is the DPP reduction
+// of each row's dot product. Raw logits (base-2 units) are parked in LDS;
+// once the partials are merged the exact probability of every slot is known
+// and the accumulated scores are updated (H2O §1 "Greedy algorithm for
+// low-cost policy", §B.2: accumulated, not averaged). The victim is the slot
+// with the smallest (score, pos) key among slots outside the recent window
+// (H2O §2 "Problem formulation": one eviction at most; §D "Cache eviction");
+// the new token then takes the victim's slot (or slot n_used while the cache
 // is not full).
+//
+// Two launch shapes share this arithmetic:
+//   decode_wave_kernel - one wave per head, persistent, double-buffered, all
+//     reductions inside the wave (DPP, v_permlane*_swap); used when there are
+//     enough heads to give every SIMD at least one wave.
+//   decode_kernel      - one 4-wave workgroup per head with an LDS merge; used
+//     for few heads with long caches.
 
 #include "h2o_device.h"
 #include "launch.h"
@@ -29,25 +34,28 @@
 namespace h2o {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-
-template <int DT, int D>
+template <int DT, int D, int WAVES>
 struct Shape {
   static constexpr int E = Elem<DT>::bytes;
   static constexpr int ROW = D * E;      // bytes per cache row
   static constexpr int LPR = ROW / 16;   // lanes per row
   static constexpr int RPU = 64 / LPR;   // rows per wave-wide load
   static constexpr int EPL = 16 / E;     // elements per lane
-  static constexpr int NP = kWaves * RPU;  // online-softmax partials per workgroup
+  static constexpr int NP = WAVES * RPU;  // online-softmax partials per workgroup
   static_assert(LPR >= 4 && LPR <= 64, "row must span 4..64 lanes");
 };
 
 // SCORED = true: the H2O step. SCORED = false: plain attention over a
 // contiguous cache of n_used rows (no new token, no scores, no eviction).
-template <int DT, int D, int UB, int PF, bool SCORED>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-  using S = Shape<DT, D>;
+//   WAVES: waves per workgroup (the head's rows are split over them)
+//   UB:    1 KiB wave-loads of K (and as many of V) issued together per batch
+//   PF:    score/pos entries per thread prefetched at kernel start
+//   MINW:  occupancy hint (waves per SIMD) for the register budget
+template <int DT, int D, int WAVES, int UB, int PF, int MINW, bool SCORED>
+__global__ __launch_bounds__(WAVES * 64, MINW) void decode_kernel(DecodeArgs a) {
+  using S = Shape<DT, D, WAVES>;
+  constexpr int kThreads = WAVES * 64;
+  constexpr int kWaves = WAVES;
   __shared__ float sm_m[S::NP];
   __shared__ float sm_l[S::NP];
   __shared__ __attribute__((aligned(16))) float sm_acc[S::NP][D];
@@ -174,11 +182,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
   const float invZ = 1.0f / Z;
 
-  if (tid < D) {
-    float o = SCORED ? fast_exp2(s_new - M) * sm_vnew[tid] : 0.f;
+  for (int dd = tid; dd < D; dd += kThreads) {
+    float o = SCORED ? fast_exp2(s_new - M) * sm_vnew[dd] : 0.f;
 #pragma unroll
-    for (int p = 0; p < S::NP; ++p) o = fmaf(sm_acc[p][tid], w[p], o);
-    a.out[size_t(head) * D + tid] = o * invZ;
+    for (int p = 0; p < S::NP; ++p) o = fmaf(sm_acc[p][dd], w[p], o);
+    a.out[size_t(head) * D + dd] = o * invZ;
   }
 
   if constexpr (SCORED) {
@@ -265,12 +273,260 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// One wave per head, persistent over heads, double-buffered.
+//
+// A workgroup is a single wave that walks heads blockIdx.x, blockIdx.x +
+// gridDim.x, ... Each head is streamed in batches of UB wave-loads of K and
+// UB of V; the loads of the next batch (possibly the next head's first one)
+// are issued before the current batch is consumed, so a wave always has one
+// batch in flight, also while it merges its partials, updates the scores and
+// picks the victim of the previous head. All reductions are inside the wave
+// (DPP and lane shuffles): there is no workgroup barrier.
+template <int DT, int D, int PF>
+struct HeadInputs {
+  uint4 q, kn, vn;
+  float sc[PF];
+  int pos[PF];
+};
+
+template <int DT, int D, int UB, int PF, int MINW, bool SCORED, bool FAIR = true>
+__global__ __launch_bounds__(64, MINW) void decode_wave_kernel(DecodeArgs a, int G) {
+  using S = Shape<DT, D, 1>;
+  extern __shared__ float sm_logit[];  // [k] logits of the current head, base-2 units
+  const int lane = threadIdx.x;
+  const int grp = lane / S::LPR;
+  const int sub = lane % S::LPR;
+  const int nu = a.n_used;
+  const int units = (nu + S::RPU - 1) / S::RPU;
+  const int nb = (units + UB - 1) / UB;  // batches per head
+  const size_t kstride = size_t(a.k) * S::ROW;
+
+  int head = blockIdx.x;
+  if (head >= G) return;
+
+  auto load_head = [&](HeadInputs<DT, D, PF>& h, int hd) {
+    const size_t off = size_t(hd) * S::ROW + sub * 16;
+    h.q = ld16(static_cast<const char*>(a.q) + off);
+    if constexpr (SCORED) {
+      h.kn = ld16(static_cast<const char*>(a.k_new) + off);
+      h.vn = ld16(static_cast<const char*>(a.v_new) + off);
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        const int slot = lane + 64 * i;
+        h.sc[i] = 0.f;
+        h.pos[i] = 0;
+        if (slot < nu) {
+          h.sc[i] = a.score[size_t(hd) * a.k + slot];
+          h.pos[i] = a.pos[size_t(hd) * a.k + slot];
+        }
+      }
+    }
+  };
+  // Loads are unconditional (rows past n_used are clamped to the last occupied
+  // row and masked out of the softmax): exec-masked loads would need their
+  // destination registers zeroed first, which forces a wait on the batch
+  // still in flight and serialises the pipeline. Only called when nu >= 1.
+  auto issue = [&](uint4 (&kb)[UB], uint4 (&vb)[UB], int hd, int b) {
+    const char* Kh = static_cast<const char*>(a.K) + hd * kstride + sub * 16;
+    const char* Vh = static_cast<const char*>(a.V) + hd * kstride + sub * 16;
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+      const int row = min((b * UB + j) * S::RPU + grp, nu - 1);
+      kb[j] = ld16(Kh + size_t(row) * S::ROW);
+      vb[j] = ld16(Vh + size_t(row) * S::ROW);
+    }
+  };
+
+  HeadInputs<DT, D, PF> cur;
+  uint4 kA[UB], vA[UB], kB[UB], vB[UB];
+  float m, l;
+  float acc[S::EPL];
+
+  auto compute = [&](const uint4 (&kc)[UB], const uint4 (&vc)[UB], int b) {
+    float s[UB];
+    float bm = kNegInf;
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+      const int row = (b * UB + j) * S::RPU + grp;
+      const float x = group_sum<S::LPR>(dot16<DT>(cur.q, kc[j])) * a.c;
+      s[j] = row < nu ? x : kNegInf;
+      bm = fmaxf(bm, s[j]);
+      if constexpr (SCORED) {
+        if (sub == 0 && row < nu) sm_logit[row] = s[j];
+      }
+    }
+    if (bm != kNegInf) {
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < S::EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+      for (int j = 0; j < UB; ++j) {
+        const float p = fast_exp2(s[j] - mn);
+        l += p;
+        float v[S::EPL];
+        Unpack<DT>::run(vc[j], v);
+#pragma unroll
+        for (int e = 0; e < S::EPL; ++e) acc[e] = fmaf(p, v[e], acc[e]);
+      }
+      m = mn;
+    }
+  };
+  auto epilogue = [&]() {
+    const size_t hrow = size_t(head) * a.k;
+    // Logits of this lane's slots do not depend on the merge: fetch them first.
+    float lg[PF];
+    if constexpr (SCORED) {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) lg[i] = (lane + 64 * i < nu) ? sm_logit[lane + 64 * i] : kNegInf;
+    }
+    float s_new = kNegInf;
+    if constexpr (SCORED) s_new = group_sum<S::LPR>(dot16<DT>(cur.q, cur.kn)) * a.c;
+    // Merge the lane-group partials: an all-reduce across groups.
+    const float M = fmaxf(across_groups<S::LPR>(m, OpMax()), s_new);
+    const float w = fast_exp2(m - M);
+    const float lw = across_groups<S::LPR>(l * w, OpAdd());
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) acc[e] = across_groups<S::LPR>(acc[e] * w, OpAdd());
+    const float w_new = fast_exp2(s_new - M);
+    const float invZ = 1.0f / (lw + w_new);
+    if (grp == 0) {
+      float o[S::EPL];
+      if constexpr (SCORED) {
+        float v[S::EPL];
+        Unpack<DT>::run(cur.vn, v);
+#pragma unroll
+        for (int e = 0; e < S::EPL; ++e) o[e] = fmaf(w_new, v[e], acc[e]) * invZ;
+      } else {
+#pragma unroll
+        for (int e = 0; e < S::EPL; ++e) o[e] = acc[e] * invZ;
+      }
+      float* op = a.out + size_t(head) * D + sub * S::EPL;
+#pragma unroll
+      for (int e = 0; e < S::EPL; e += 4)
+        *reinterpret_cast<float4*>(op + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+    }
+    if constexpr (SCORED) {
+      const float p_new = w_new * invZ;
+      const bool full = nu == a.k;
+      const int lim = a.t - a.k_recent;
+      float* sc_g = a.score + hrow;
+      int32_t* pos_g = a.pos + hrow;
+      uint64_t best = ~0ull;
+      int best_slot = -1;
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        const int slot = lane + 64 * i;
+        if (slot < nu) {
+          const float sc = cur.sc[i] + fast_exp2(lg[i] - M) * invZ;
+          sc_g[slot] = sc;
+          if (full && cur.pos[i] <= lim) {
+            const uint64_t key = score_pos_key(sc, cur.pos[i]);
+            if (key < best) {
+              best = key;
+              best_slot = slot;
+            }
+          }
+        }
+      }
+      for (int slot = lane + 64 * PF; slot < nu; slot += 64) {
+        const float sc = sc_g[slot] + fast_exp2(sm_logit[slot] - M) * invZ;
+        const int ps = pos_g[slot];
+        sc_g[slot] = sc;
+        if (full && ps <= lim) {
+          const uint64_t key = score_pos_key(sc, ps);
+          if (key < best) {
+            best = key;
+            best_slot = slot;
+          }
+        }
+      }
+      int victim = nu;
+      int evicted = -1;
+      if (full) {
+        const uint64_t gmin = wave_min_u64(best);
+        // Keys are unique (positions are), so exactly one lane holds the minimum.
+        const uint64_t owners = __ballot(best == gmin && gmin != ~0ull);
+        if (owners) {
+          victim = __builtin_amdgcn_readlane(best_slot, __ffsll((unsigned long long)owners) - 1);
+          evicted = int(uint32_t(gmin & 0xffffffffu));
+        } else {
+          victim = -1;  // no eligible slot: the caller's state is inconsistent
+          evicted = -2;
+        }
+      }
+      if (victim >= 0) {
+        if (lane == victim % 64) {
+          sc_g[victim] = p_new;
+          pos_g[victim] = a.t;
+        }
+        if (grp == 0) {
+          st16(static_cast<char*>(a.K_w) + (hrow + victim) * S::ROW + sub * 16, cur.kn);
+          st16(static_cast<char*>(a.V_w) + (hrow + victim) * S::ROW + sub * 16, cur.vn);
+        }
+      }
+      if (lane == 0) a.evicted[head] = evicted;
+    }
+  };
+
+  for (; head < G; head += gridDim.x) {
+    load_head(cur, head);
+    m = kNegInf;
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < S::EPL; ++e) acc[e] = 0.f;
+    // Two batches in flight: B is issued before A is consumed, A before B.
+    // Issues are unconditional so that every path through the loop has the
+    // same loads outstanding (the wait counts stay exact); a batch past the
+    // end re-reads the last occupied row, an L2 hit, and is masked out.
+    if (nb > 0) {
+      issue(kA, vA, head, 0);
+      for (int b = 0; b < nb; b += 2) {
+        // Fair share of the memory pipe between the waves of a SIMD: the
+        // arbiter favours the oldest wave, which would stream its head first
+        // and leave the others starved until the end. Priority falls as a
+        // wave's progress rises, so lagging waves issue first.
+        if constexpr (FAIR) set_wave_priority(3 - (4 * b) / nb);
+        issue(kB, vB, head, b + 1);
+        compute(kA, vA, b);
+        issue(kA, vA, head, b + 2);
+        compute(kB, vB, b + 1);
+      }
+    }
+    epilogue();
+  }
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
 template <int DT, int D, bool SCORED>
 hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
-  constexpr int UB = 8;
-  constexpr int PF = 4;
   const size_t shmem = SCORED ? size_t(a.k) * sizeof(float) : 0;
-  hipLaunchKernelGGL((decode_kernel<DT, D, UB, PF, SCORED>), dim3(G), dim3(kThreads), shmem, s, a);
+  constexpr int WMINW = 2;  // waves per SIMD the wave kernel is built for
+  const int resident = cu_count() * 4 * WMINW;
+  if (G >= resident / 2) {
+    constexpr int UB = 8, PF = 4;
+    const int grid = G < resident ? G : resident;
+    hipLaunchKernelGGL((decode_wave_kernel<DT, D, UB, PF, WMINW, SCORED>), dim3(grid), dim3(64), shmem, s, a, G);
+  } else {
+    // Few heads: spread each head over a 4-wave workgroup instead.
+    constexpr int WAVES = 4, UB = 8, PF = 4, MINW = 1;
+    hipLaunchKernelGGL((decode_kernel<DT, D, WAVES, UB, PF, MINW, SCORED>), dim3(G), dim3(WAVES * 64), shmem,
+                       s, a);
+  }
   return hipGetLastError();
 }
 

@@ -113,6 +113,82 @@ template <int N> __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Wave issue priority (s_setprio takes an immediate, hence the switch).
+__device__ __forceinline__ void set_wave_priority(int p) {
+  switch (p) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
+// ---- cross-row exchanges without LDS (gfx950) --------------------------------
+// v_permlane16_swap / v_permlane32_swap exchange rows of 16 lanes (odd rows
+// with even rows) and the two 32-lane halves. Called with the same value as
+// both operands they return, in every lane, the pair {even-side, odd-side}
+// value in a fixed order, so a commutative combine of the pair is bitwise
+// identical in both partner lanes.
+struct LanePair {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ LanePair swap16(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return {r[0], r[1]};
+}
+__device__ __forceinline__ LanePair swap32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return {r[0], r[1]};
+}
+constexpr int kRowRor8 = 0x128;  // lane i <- lane (i + 8) mod 16 within each row
+
+// Combine values across the lane groups of N consecutive lanes (N in
+// {8, 16, 32}): lanes at the same position in every group end with the same
+// result. OP is a commutative binary functor on floats.
+template <int N, class OP> __device__ __forceinline__ float across_groups(float x, OP op) {
+  static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  if constexpr (N <= 8) x = op(x, dpp<kRowRor8>(x));
+  if constexpr (N <= 16) {
+    const LanePair r = swap16(__float_as_uint(x));
+    x = op(__uint_as_float(r.lo), __uint_as_float(r.hi));
+  }
+  if constexpr (N <= 32) {
+    const LanePair r = swap32(__float_as_uint(x));
+    x = op(__uint_as_float(r.lo), __uint_as_float(r.hi));
+  }
+  return x;
+}
+struct OpAdd {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+template <int CTRL> __device__ __forceinline__ uint64_t dpp64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(x)), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(x >> 32)), CTRL, 0xF, 0xF, false);
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t min64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// Minimum of a 64-bit key over the whole wave, in every lane (no LDS).
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t k) {
+  k = min64(k, dpp64<kQuadSwap1>(k));
+  k = min64(k, dpp64<kQuadSwap2>(k));
+  k = min64(k, dpp64<kRowHalfMirror>(k));
+  k = min64(k, dpp64<kRowMirror>(k));
+  {
+    const LanePair lo = swap16(uint32_t(k)), hi = swap16(uint32_t(k >> 32));
+    k = min64((uint64_t(hi.lo) << 32) | lo.lo, (uint64_t(hi.hi) << 32) | lo.hi);
+  }
+  {
+    const LanePair lo = swap32(uint32_t(k)), hi = swap32(uint32_t(k >> 32));
+    k = min64((uint64_t(hi.lo) << 32) | lo.lo, (uint64_t(hi.hi) << 32) | lo.hi);
+  }
+  return k;
+}
+
 // Order-preserving key of a non-negative float and a position: the smallest
 // key is the smallest score, and among equal scores the smallest position.
 __device__ __forceinline__ uint64_t score_pos_key(float score, int32_t pos) {
