@@ -45,6 +45,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="opt6.7b_layer")
     p.add_argument("--layers", type=int, default=4, help="independent layer caches decoded in rotation")
+    p.add_argument("--decode-steps", type=int, default=None,
+                   help="decode steps per bench step (default: the workload's own count; for profiling runs)")
     p.add_argument("--cpu-heads", type=int, default=256, help="heads in the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-single-layer", action="store_true")
@@ -131,6 +133,8 @@ def main():
 
     lib = load_library()
     wl = WORKLOADS[args.workload]
+    if args.decode_steps is not None:
+        wl = wl.with_(steps=max(1, min(args.decode_steps, wl.steps)))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]

@@ -8,7 +8,8 @@
 // softmax over keys j <= i, H2O §D "Recursive attention") is reduced to its
 // column sums c_j, the accumulated attention each prompt token receives
 // (H2O §1, §4.1). c needs each row's final normaliser, so QK^T is formed
-// twice, both times on MFMA (v_mfma_f32_32x32x16_{bf16,f16}):
+// twice, both times on MFMA (v_mfma_f32_32x32x16_{bf16,f16}), with the operand
+// shared by a workgroup staged through LDS:
 //
 //   pass 1 (rowlse):  lse2_i = log2 sum_j 2^(c * s_ij), keys streamed per query
 //                     block; the tile is computed transposed (keys x queries)
@@ -57,71 +58,130 @@ template <> struct MfmaOp<DT_F16> {
 // D[8*(j/4) + 4*(l/32) + j%4][l % 32].
 __device__ __forceinline__ int mfma_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
 
-constexpr int kWaveCols = 64;                 // queries (pass 1) or keys (pass 2) per wave
-constexpr int kBlockCols = 4 * kWaveCols;     // per workgroup
-
-// ---------------------------------------------------------------- pass 1 (MFMA)
+// ---------------------------------------------------------------- LDS-staged passes
+// Both passes form 64x64 score tiles per wave per iteration (4 accumulators of
+// 32x32, 32 MFMAs). The operand that all four waves of a workgroup share (K
+// rows in pass 1, Q rows in pass 2) is staged through LDS in 64-row tiles:
+// each thread fetches 1/256 of the next tile into registers while the current
+// tile is consumed, then writes it to the other LDS buffer (one barrier per
+// tile). Rows are padded by 16 bytes in LDS so that the 32 rows one MFMA
+// operand read touches fall into distinct banks.
 template <int DT, int D>
-__global__ __launch_bounds__(256) void rowlse_mfma(PrefillArgs a, int nblk, int G, int ld_lse) {
-  constexpr int E = Elem<DT>::bytes, ROW = D * E, KS = D / 16;
+struct Tile64 {
+  static constexpr int E = Elem<DT>::bytes;
+  static constexpr int ROW = D * E;       // bytes per row in global memory
+  static constexpr int CH = ROW / 16;     // 16-byte chunks per row
+  static constexpr int RS = ROW + 16;     // padded LDS row stride
+  static constexpr int BYTES = 64 * RS;   // one 64-row tile
+  static constexpr int CPT = CH / 4;      // chunks per thread (4 threads per row)
+  static constexpr int KS = D / 16;       // MFMA k-steps per row
+
+  // Fetch rows [r0, r0 + 64) (clamped to n - 1) of `src` into registers.
+  __device__ __forceinline__ static void fetch(uint4 (&r)[CPT], const char* src, int r0, int n) {
+    const int t = threadIdx.x;
+    const int row = min(r0 + (t >> 2), n - 1);
+    const char* p = src + size_t(row) * ROW + (t & 3) * CPT * 16;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) r[i] = ld16(p + i * 16);
+  }
+  __device__ __forceinline__ static void store(char* lds, const uint4 (&r)[CPT]) {
+    const int t = threadIdx.x;
+    char* p = lds + (t >> 2) * RS + (t & 3) * CPT * 16;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) *reinterpret_cast<uint4*>(p + i * 16) = r[i];
+  }
+  // MFMA operand fragment: row (32*blk + lane%32), k-step ks.
+  __device__ __forceinline__ static uint4 frag(const char* lds, int blk, int ks, int lane) {
+    return *reinterpret_cast<const uint4*>(lds + (blk * 32 + (lane & 31)) * RS + (ks * 2 + (lane >> 5)) * 16);
+  }
+};
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Pass 1: lse2_i = log2 sum_{j<=i} 2^(c*s_ij). Workgroup = 256 queries (64 per
+// wave); keys streamed in 64-row LDS tiles. The transposed tile (keys x
+// queries) gives each lane one query column, so the row statistics are
+// in-lane until the final merge of the two lane halves.
+template <int DT, int D>
+__global__ __launch_bounds__(256, 2) void rowlse_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
+  using T = Tile64<DT, D>;
+  __shared__ __attribute__((aligned(16))) char lds[2][T::BYTES];
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
-  if (L >= G * nblk) return;
+  if (L >= G * nblk) return;  // uniform over the workgroup
   const int head = L / nblk;
   const int qb = nblk - 1 - L % nblk;  // longest causal extent first
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lh = lane >> 5;
   const int n = a.n;
-  const int q0 = qb * kBlockCols + wave * kWaveCols;
-  if (q0 >= n) return;
-  const int lr = lane & 31, lh = lane >> 5;
-  const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * ROW;
-  const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * ROW;
+  const int wg_q0 = qb * 256;
+  const int q0 = wg_q0 + wave * 64;
+  const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
+  const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
+  const float c = a.c;
 
-  uint4 qf[2][KS];
+  uint4 qf[2][T::KS];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const int r = min(q0 + cb * 32 + lr, n - 1);
+    const int r = min(q0 + cb * 32 + (lane & 31), n - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * ROW + (ks * 16 + lh * 8) * E);
+    for (int ks = 0; ks < T::KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
   }
-  const float c = a.c;
   float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
-  const int qlast = min(q0 + kWaveCols, n) - 1;
-  const int ntiles = qlast / 32 + 1;
+  const int ntiles = min(wg_q0 + 255, n - 1) / 64 + 1;
+  uint4 nx[T::CPT];
+  T::fetch(nx, Kh, 0, n);
+  T::store(lds[0], nx);
+  __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int key0 = kt * 32;
-    const int kr = min(key0 + lr, n - 1);
-    uint4 kf[KS];
+    if (kt + 1 < ntiles) T::fetch(nx, Kh, (kt + 1) * 64, n);
+    const char* buf = lds[kt & 1];
+    const int key0 = kt * 64;
+    if (key0 <= min(q0 + 63, n - 1)) {  // some key of the tile is visible to this wave
+      f32x16 acc[2][2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = ld16(Kh + size_t(kr) * ROW + (ks * 16 + lh * 8) * E);
-    f32x16 acc[2];
+      for (int kb = 0; kb < 2; ++kb) {
+        uint4 af[T::KS];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      acc[cb] = f32x16{};
+        for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, kb, ks, lane);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc[cb] = MfmaOp<DT>::run(kf[ks], qf[cb][ks], acc[cb]);
-    }
-    // acc[cb][j] = s(query q0 + 32cb + lr, key key0 + mfma_row(j))
+        for (int cb = 0; cb < 2; ++cb) {
+          acc[kb][cb] = f32x16{};
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int qi = q0 + cb * 32 + lr;
-      const bool diag = key0 + 31 > q0 + cb * 32;
-      float s[16];
-      float tm = kNegInf;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        s[j] = (diag && key0 + mfma_row(j, lane) > qi) ? kNegInf : acc[cb][j];
-        tm = fmaxf(tm, s[j]);
+          for (int ks = 0; ks < T::KS; ++ks) acc[kb][cb] = MfmaOp<DT>::run(af[ks], qf[cb][ks], acc[kb][cb]);
+        }
       }
-      const float mn = fmaxf(m[cb], tm);
-      if (mn != kNegInf) {
-        const float mnc = mn * c;
-        float t = 0.f;
+      // acc[kb][cb][j] = s(query q0 + 32cb + lane%32, key key0 + 32kb + mfma_row(j))
 #pragma unroll
-        for (int j = 0; j < 16; ++j) t += fast_exp2(fmaf(s[j], c, -mnc));
-        l[cb] = fmaf(l[cb], fast_exp2((m[cb] - mn) * c), t);
-        m[cb] = mn;
+      for (int cb = 0; cb < 2; ++cb) {
+        const int qi = q0 + cb * 32 + (lane & 31);
+        if (key0 + 63 > q0 + cb * 32) {  // tile reaches past some query of this block: mask
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][cb][j] = kNegInf;
+        }
+        float tm = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][cb][j], acc[0][cb][j + 1]);
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
+        const float mn = fmaxf(m[cb], tm);
+        if (mn != kNegInf) {
+          const float mnc = mn * c;
+          float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            t0 += fast_exp2(fmaf(acc[0][cb][j], c, -mnc));
+            t1 += fast_exp2(fmaf(acc[1][cb][j], c, -mnc));
+          }
+          l[cb] = fmaf(l[cb], fast_exp2((m[cb] - mn) * c), t0 + t1);
+          m[cb] = mn;
+        }
       }
     }
+    if (kt + 1 < ntiles) T::store(lds[(kt + 1) & 1], nx);
+    __syncthreads();
   }
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -129,84 +189,124 @@ __global__ __launch_bounds__(256) void rowlse_mfma(PrefillArgs a, int nblk, int 
     const float lo = __shfl_xor(l[cb], 32);
     const float M = fmaxf(m[cb], mo);
     const float Lsum = l[cb] * fast_exp2((m[cb] - M) * c) + lo * fast_exp2((mo - M) * c);
-    const int qi = q0 + cb * 32 + lr;
+    const int qi = q0 + cb * 32 + (lane & 31);
     if (lh == 0 && qi < n) a.lse2[size_t(head) * ld_lse + qi] = M * c + fast_log2(Lsum);
   }
 }
 
-// ---------------------------------------------------------------- pass 2 (MFMA)
+// Pass 2: c_j = sum_{i>=j} 2^(c*s_ij - lse2_i). Workgroup = 256 keys (64 per
+// wave, held in registers as MFMA B operands); queries streamed in 64-row LDS
+// tiles together with their lse2. Each lane owns one key column; the tile
+// partial of 32 values is added with compensation.
 template <int DT, int D>
-__global__ __launch_bounds__(256) void colsum_mfma(PrefillArgs a, int nblk, int G, int ld_lse) {
-  constexpr int E = Elem<DT>::bytes, ROW = D * E, KS = D / 16;
+__global__ __launch_bounds__(256, 2) void colsum_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
+  using T = Tile64<DT, D>;
+  __shared__ __attribute__((aligned(16))) char lds[2][T::BYTES];
+  __shared__ __attribute__((aligned(16))) float lds_lse[2][64];
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
   if (L >= G * nblk) return;
   const int head = L / nblk;
-  const int kb = L % nblk;  // smallest key block = most query tiles, first
+  const int kblk = L % nblk;  // smallest key block = most query tiles, first
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lh = lane >> 5;
   const int n = a.n;
-  const int k0 = kb * kBlockCols + wave * kWaveCols;
-  if (k0 >= n) return;
-  const int lr = lane & 31, lh = lane >> 5;
-  const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * ROW;
-  const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * ROW;
+  const int wg_k0 = kblk * 256;
+  const int k0 = wg_k0 + wave * 64;
+  const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
+  const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
   const float* lse = a.lse2 + size_t(head) * ld_lse;
-
-  uint4 kf[2][KS];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int r = min(k0 + cb * 32 + lr, n - 1);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[cb][ks] = ld16(Kh + size_t(r) * ROW + (ks * 16 + lh * 8) * E);
-  }
   const float c = a.c;
+
+  uint4 kf[2][T::KS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = min(k0 + kb * 32 + (lane & 31), n - 1);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) kf[kb][ks] = ld16(Kh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
+  }
   float sum[2] = {0.f, 0.f}, comp[2] = {0.f, 0.f};
-  const int nqt = (n + 31) / 32;
-  for (int qt = k0 / 32; qt < nqt; ++qt) {
-    const int qrow0 = qt * 32;
-    const int qr = min(qrow0 + lr, n - 1);
-    uint4 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(Qh + size_t(qr) * ROW + (ks * 16 + lh * 8) * E);
-    float lq[16];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float4 v = *reinterpret_cast<const float4*>(lse + qrow0 + 8 * jj + 4 * lh);
-      lq[4 * jj] = v.x;
-      lq[4 * jj + 1] = v.y;
-      lq[4 * jj + 2] = v.z;
-      lq[4 * jj + 3] = v.w;
+  const int t0 = wg_k0 / 64;
+  const int ntiles = (n + 63) / 64;
+  uint4 nx[T::CPT];
+  float nl = 0.f;
+  // Rows past the prompt get lse = +inf, so their terms are exp2(-inf) = 0
+  // without a per-element test.
+  auto fetch = [&](int qt) {
+    T::fetch(nx, Qh, qt * 64, n);
+    if (threadIdx.x < 64) {
+      const int q = qt * 64 + threadIdx.x;
+      nl = q < n ? lse[q] : __builtin_huge_valf();
     }
-    f32x16 acc[2];
+  };
+  auto store = [&](int buf) {
+    T::store(lds[buf], nx);
+    if (threadIdx.x < 64) lds_lse[buf][threadIdx.x] = nl;
+  };
+  fetch(t0);
+  store(0);
+  __syncthreads();
+  for (int qt = t0; qt < ntiles; ++qt) {
+    const int cur = (qt - t0) & 1;
+    if (qt + 1 < ntiles) fetch(qt + 1);
+    const int qrow0 = qt * 64;
+    if (qrow0 + 63 >= k0 && k0 < n) {  // some query of the tile sees a key of this wave
+      const char* buf = lds[cur];
+      f32x16 acc[2][2];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      acc[cb] = f32x16{};
+      for (int qb = 0; qb < 2; ++qb) {
+        uint4 af[T::KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc[cb] = MfmaOp<DT>::run(qf[ks], kf[cb][ks], acc[cb]);
-    }
-    // acc[cb][j] = s(query qrow0 + mfma_row(j), key k0 + 32cb + lr)
+        for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, qb, ks, lane);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int kj = k0 + cb * 32 + lr;
-      const bool edge = (qrow0 < k0 + cb * 32 + 31) || (qrow0 + 31 >= n);
-      float t = 0.f;
+        for (int kb = 0; kb < 2; ++kb) {
+          acc[qb][kb] = f32x16{};
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qi = qrow0 + mfma_row(j, lane);
-        const float x = fast_exp2(fmaf(acc[cb][j], c, -lq[j]));
-        t += (edge && (qi < kj || qi >= n)) ? 0.f : x;
+          for (int ks = 0; ks < T::KS; ++ks) acc[qb][kb] = MfmaOp<DT>::run(af[ks], kf[kb][ks], acc[qb][kb]);
+        }
       }
-      // compensated accumulation across query tiles
-      const float y = t - comp[cb];
-      const float s2 = sum[cb] + y;
-      comp[cb] = (s2 - sum[cb]) - y;
-      sum[cb] = s2;
+      // acc[qb][kb][j] = s(query qrow0 + 32qb + mfma_row(j), key k0 + 32kb + lane%32)
+      float lq[2][16];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float4 v = *reinterpret_cast<const float4*>(&lds_lse[cur][qb * 32 + 8 * jj + 4 * lh]);
+          lq[qb][4 * jj] = v.x;
+          lq[qb][4 * jj + 1] = v.y;
+          lq[qb][4 * jj + 2] = v.z;
+          lq[qb][4 * jj + 3] = v.w;
+        }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kj = k0 + kb * 32 + (lane & 31);
+        if (qrow0 < k0 + kb * 32 + 31) {  // diagonal tile: queries before the key see nothing
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              acc[qb][kb][j] = qrow0 + qb * 32 + mfma_row(j, lane) < kj ? kNegInf : acc[qb][kb][j];
+        }
+        float t = 0.f, t2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          t += fast_exp2(fmaf(acc[0][kb][j], c, -lq[0][j]));
+          t2 += fast_exp2(fmaf(acc[1][kb][j], c, -lq[1][j]));
+        }
+        t += t2;
+        const float y = t - comp[kb];
+        const float s2 = sum[kb] + y;
+        comp[kb] = (s2 - sum[kb]) - y;
+        sum[kb] = s2;
+      }
     }
+    if (qt + 1 < ntiles) store(cur ^ 1);
+    __syncthreads();
   }
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const float mine = sum[cb] - comp[cb];
+  for (int kb = 0; kb < 2; ++kb) {
+    const float mine = sum[kb] - comp[kb];
     const float other = __shfl_xor(mine, 32);
-    const int kj = k0 + cb * 32 + lr;
+    const int kj = k0 + kb * 32 + (lane & 31);
     if (lh == 0 && kj < n) a.colsum[size_t(head) * n + kj] = mine + other;
   }
 }
@@ -399,10 +499,10 @@ hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((rowlse_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
     hipLaunchKernelGGL((colsum_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
   } else {
-    const int nblk = (a.n + kBlockCols - 1) / kBlockCols;
+    const int nblk = (a.n + 255) / 256;
     const int grid = pad8(G * nblk);
-    hipLaunchKernelGGL((rowlse_mfma<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
-    hipLaunchKernelGGL((colsum_mfma<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
+    hipLaunchKernelGGL((rowlse_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
+    hipLaunchKernelGGL((colsum_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
   }
   hipLaunchKernelGGL((select_gather<DT, D>), dim3(G), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
