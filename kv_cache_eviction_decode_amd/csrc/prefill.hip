@@ -73,22 +73,31 @@ struct Tile64 {
   static constexpr int CH = ROW / 16;     // 16-byte chunks per row
   static constexpr int RS = ROW + 16;     // padded LDS row stride
   static constexpr int BYTES = 64 * RS;   // one 64-row tile
-  static constexpr int CPT = CH / 4;      // chunks per thread (4 threads per row)
+  static constexpr int CPT = CH / 4;      // chunks per thread (256 threads, 64 rows)
+  static constexpr int RPI = 64 / CH;     // rows one wave-wide 16-byte access covers
   static constexpr int KS = D / 16;       // MFMA k-steps per row
+
+  // Thread (wave w, lane l) moves chunk l % CH of rows 16w + i*RPI + l / CH:
+  // each wave-wide access is 1 KiB of consecutive rows in global memory, and
+  // consecutive lanes write consecutive 16-byte chunks of one LDS row (no
+  // bank conflicts).
+  __device__ __forceinline__ static int my_row(int i) {
+    return (threadIdx.x >> 6) * 16 + i * RPI + (threadIdx.x & 63) / CH;
+  }
+  __device__ __forceinline__ static int my_chunk() { return (threadIdx.x & 63) % CH; }
 
   // Fetch rows [r0, r0 + 64) (clamped to n - 1) of `src` into registers.
   __device__ __forceinline__ static void fetch(uint4 (&r)[CPT], const char* src, int r0, int n) {
-    const int t = threadIdx.x;
-    const int row = min(r0 + (t >> 2), n - 1);
-    const char* p = src + size_t(row) * ROW + (t & 3) * CPT * 16;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) r[i] = ld16(p + i * 16);
+    for (int i = 0; i < CPT; ++i) {
+      const int row = min(r0 + my_row(i), n - 1);
+      r[i] = ld16(src + size_t(row) * ROW + my_chunk() * 16);
+    }
   }
   __device__ __forceinline__ static void store(char* lds, const uint4 (&r)[CPT]) {
-    const int t = threadIdx.x;
-    char* p = lds + (t >> 2) * RS + (t & 3) * CPT * 16;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) *reinterpret_cast<uint4*>(p + i * 16) = r[i];
+    for (int i = 0; i < CPT; ++i)
+      *reinterpret_cast<uint4*>(lds + my_row(i) * RS + my_chunk() * 16) = r[i];
   }
   // MFMA operand fragment: row (32*blk + lane%32), k-step ks.
   __device__ __forceinline__ static uint4 frag(const char* lds, int blk, int ks, int lane) {
@@ -97,6 +106,12 @@ struct Tile64 {
 };
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Wait for every outstanding vector-memory load. Used once, after the
+// register-resident MFMA operands are loaded: without it the wait-count pass
+// cannot tell at the tile loop's header that those loads are done and waits
+// for the next tile's prefetch inside the MFMA chain, exposing its latency.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Pass 1: lse2_i = log2 sum_{j<=i} 2^(c*s_ij). Workgroup = 256 queries (64 per
 // wave); keys streamed in 64-row LDS tiles. The transposed tile (keys x
@@ -126,6 +141,7 @@ __global__ __launch_bounds__(256, 2) void rowlse_lds(PrefillArgs a, int nblk, in
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
   }
+  wait_vmem_all();
   float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
   const int ntiles = min(wg_q0 + 255, n - 1) / 64 + 1;
   uint4 nx[T::CPT];
@@ -224,6 +240,7 @@ __global__ __launch_bounds__(256, 2) void colsum_lds(PrefillArgs a, int nblk, in
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) kf[kb][ks] = ld16(Kh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
   }
+  wait_vmem_all();
   float sum[2] = {0.f, 0.f}, comp[2] = {0.f, 0.f};
   const int t0 = wg_k0 / 64;
   const int ntiles = (n + 63) / 64;
