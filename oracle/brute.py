@@ -21,7 +21,13 @@ a mistake in one does not repeat in the other:
   exhaustive search pins it);
 * the eviction is the set-function form of H2O §D "Cache eviction": among the
   positions that may leave, remove the one whose removal leaves the cache
-  with the largest total score.
+  with the largest total value.
+
+Values per policy (see the oracle): accumulated score; averaged score (the
+accumulated score over the count of queries that attended to the token,
+counted here by an explicit per-position counter rather than a formula); or
+minus the position (StreamingLLM's sinks plus window). With no recent window
+(k_recent = 0) the new token is among the positions that may leave.
 """
 from __future__ import annotations
 
@@ -33,7 +39,8 @@ def _dot(a, b):
     return sum(float(x) * float(y) for x, y in zip(a, b))
 
 
-def brute_run(Q, K, V, q_dec, k_dec, v_dec, k_heavy: int, k_recent: int, scale: float):
+def brute_run(Q, K, V, q_dec, k_dec, v_dec, k_heavy: int, k_recent: int, scale: float,
+              policy: str = "accumulated"):
     """Replay prefill plus len(q_dec) decode steps for ONE head.
 
     Returns a dict with ``colsum`` (prompt column sums), ``kept`` (positions
@@ -47,6 +54,16 @@ def brute_run(Q, K, V, q_dec, k_dec, v_dec, k_heavy: int, k_recent: int, scale: 
     vals = [list(map(float, r)) for r in V] + [list(map(float, r)) for r in v_dec]
     d = len(keys[0]) if keys else 0
     acc = [0.0] * (n + T)
+    seen = [0] * (n + T)  # number of queries that attended to each position
+
+    def worth(j):
+        if policy == "accumulated":
+            return acc[j]
+        if policy == "averaged":
+            return acc[j] / seen[j]
+        if policy == "position":
+            return -float(j)
+        raise ValueError(policy)
 
     # Prefill: every prompt query attends over all prompt keys up to itself.
     for i in range(n):
@@ -54,6 +71,7 @@ def brute_run(Q, K, V, q_dec, k_dec, v_dec, k_heavy: int, k_recent: int, scale: 
         z = sum(w)
         for j in range(i + 1):
             acc[j] += w[j] / z
+            seen[j] += 1
     colsum = acc[:n]
 
     if n <= k:
@@ -61,9 +79,9 @@ def brute_run(Q, K, V, q_dec, k_dec, v_dec, k_heavy: int, k_recent: int, scale: 
     else:
         recent = set(range(n - k_recent, n))
         cand = range(n - k_recent)
-        # Largest total; among equal totals prefer later positions.
+        # Largest total value; among equal totals prefer later positions.
         best = max(combinations(cand, k_heavy),
-                   key=lambda S: (sum(acc[j] for j in S), sorted(S, reverse=True)))
+                   key=lambda S: (sum(worth(j) for j in S), sorted(S, reverse=True)))
         alive = set(best) | recent
     kept = set(alive)
 
@@ -77,6 +95,7 @@ def brute_run(Q, K, V, q_dec, k_dec, v_dec, k_heavy: int, k_recent: int, scale: 
         outs.append([sum(probs[a] * vals[j][c] for a, j in enumerate(members)) for c in range(d)])
         for a, j in enumerate(members):
             acc[j] += probs[a]
+            seen[j] += 1
         if len(alive) < k:
             alive.add(t)
             evicted.append(-1)
@@ -85,7 +104,7 @@ def brute_run(Q, K, V, q_dec, k_dec, v_dec, k_heavy: int, k_recent: int, scale: 
         leavers = [v for v in S if v <= t - k_recent]
 
         def total_without(v):
-            return sum(acc[u] for u in S if u != v)
+            return sum(worth(u) for u in S if u != v)
 
         # Largest remaining total; on equal totals the older position leaves.
         out_pos = max(leavers, key=lambda v: (total_without(v), -v))

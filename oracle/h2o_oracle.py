@@ -39,9 +39,23 @@ Readings where the page is silent (the design notes list them all):
   [k_heavy, k), and a decode step writes into the victim's slot (or slot n_used
   while the cache is not yet full).
 
+Policies (the variants the page compares H2O with or reports as worse):
+  "accumulated" (H2O): a token's value is its accumulated score;
+  "averaged": its accumulated score divided by the number of queries that
+      have attended to it so far (H2O §B.2 "Previous Attempts" reports this
+      variant as worse);
+  "position": its value is minus its position, so the earliest tokens stay
+      (attention sinks) and the oldest token outside them leaves, which is
+      StreamingLLM's sink-plus-window cache (Discoveries (cursor 150),
+      StreamingLLM abstract; compared in H2O §C.1 "Long-context generation").
+  k_heavy = 0 is the "Local" recent-window baseline and k_recent = 0 the
+  heavy-hitter-only ablation (H2O §5 "Ablation and Extended Evaluations");
+  with k_recent = 0 the new token itself competes and may be the one evicted.
+
 Pins: brute force on tiny inputs, the q = 0 closed form, textbook special
-cases (full cache = causal attention, k_heavy = 0 = sliding window), the
-budget-3 illustration of H2O §4.1 and invariants; see tests/test_oracle_pins.py.
+cases (full cache = causal attention, k_heavy = 0 = sliding window, the
+position policy = sink-plus-window attention), the budget-3 illustration of
+H2O §4.1 and invariants; see tests/test_oracle_pins.py.
 """
 from __future__ import annotations
 
@@ -49,8 +63,28 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["causal_attention_probs", "prefill_column_sums", "select_prefill",
-           "eligible_slots", "choose_victim", "H2OOracle", "PrefillResult", "StepResult"]
+__all__ = ["causal_attention_probs", "prefill_column_sums", "select_prefill", "retention_value",
+           "eligible_slots", "choose_victim", "H2OOracle", "PrefillResult", "StepResult", "POLICIES"]
+
+POLICIES = ("accumulated", "averaged", "position")
+
+
+def retention_value(score, pos, t, policy: str):
+    """How much a cached token is worth keeping at step t (larger = keep).
+
+    accumulated: the accumulated score (H2O §1, §4.1); averaged: that score
+    over the number of queries t - pos + 1 that have attended to the token
+    (H2O §B.2); position: -pos (earliest tokens are kept, StreamingLLM).
+    """
+    score = np.asarray(score, np.float64)
+    pos = np.asarray(pos)
+    if policy == "accumulated":
+        return score
+    if policy == "averaged":
+        return score / (t - pos + 1)
+    if policy == "position":
+        return -pos.astype(np.float64)
+    raise ValueError(f"unknown policy {policy!r}")
 
 
 def causal_attention_probs(Q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
@@ -80,15 +114,16 @@ def prefill_column_sums(Q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarra
     return causal_attention_probs(Q, K, scale).sum(axis=0)
 
 
-def select_prefill(c: np.ndarray, k_heavy: int, k_recent: int):
+def select_prefill(c: np.ndarray, k_heavy: int, k_recent: int, policy: str = "accumulated"):
     """Positions kept after prefill, in slot order, and the selection margin.
 
     H2O §A "Pseudocode": a prompt long enough is reduced to heavy hitters plus
     recent tokens; §A "System Details": heavy hitters first, recent tokens last.
-    Candidates for the heavy part are the positions before the recent window.
-    Keys compare as (c_j, j), so on equal scores the later position is kept.
-    The margin is the relative gap between the smallest kept candidate score
-    and the largest dropped one (inf when nothing is dropped).
+    Candidates for the heavy part are the positions before the recent window;
+    they are ranked by (retention value at the last prompt row, position), so
+    on equal values the later position is kept. The margin is the relative
+    gap between the smallest kept candidate value and the largest dropped one
+    (inf when nothing is dropped or the values cannot tie).
     """
     c = np.asarray(c, np.float64)
     n = c.shape[0]
@@ -96,12 +131,13 @@ def select_prefill(c: np.ndarray, k_heavy: int, k_recent: int):
     if n <= k:
         return np.arange(n, dtype=np.int64), np.inf
     recent = np.arange(n - k_recent, n, dtype=np.int64)
-    candidates = list(range(n - k_recent))
-    ranked = sorted(candidates, key=lambda j: (c[j], j), reverse=True)
+    candidates = np.arange(n - k_recent)
+    val = retention_value(c[candidates], candidates, n - 1, policy)
+    ranked = sorted(range(candidates.size), key=lambda j: (val[j], j), reverse=True)
     heavy = np.array(sorted(ranked[:k_heavy]), dtype=np.int64)
     margin = np.inf
-    if 0 < k_heavy < len(ranked):
-        lo_kept, hi_dropped = c[ranked[k_heavy - 1]], c[ranked[k_heavy]]
+    if 0 < k_heavy < len(ranked) and policy != "position":
+        lo_kept, hi_dropped = val[ranked[k_heavy - 1]], val[ranked[k_heavy]]
         margin = (lo_kept - hi_dropped) / lo_kept if lo_kept > 0 else 0.0
     return np.concatenate([heavy, recent]), margin
 
@@ -115,23 +151,25 @@ def eligible_slots(pos: np.ndarray, t: int, k_recent: int) -> np.ndarray:
     return (pos >= 0) & (pos <= t - k_recent)
 
 
-def choose_victim(score: np.ndarray, pos: np.ndarray, eligible: np.ndarray):
-    """Per head, the eligible slot with the smallest (score, pos), and the eviction margin.
+def choose_victim(value: np.ndarray, pos: np.ndarray, eligible: np.ndarray, exact: bool = False):
+    """Per head, the eligible candidate with the smallest (value, pos), and the eviction margin.
 
     H2O §4.1 and §D "Cache eviction": the lowest accumulated score leaves.
-    Ties on the score evict the older position. The margin is
-    (second smallest - smallest) / second smallest over the eligible scores.
+    Ties on the value evict the older position. The margin is
+    (second smallest - smallest) / second smallest over the eligible values
+    (inf when `exact`: the values are distinct integers).
     """
-    G = score.shape[0]
-    masked = np.where(eligible, score, np.inf)
+    G = value.shape[0]
+    masked = np.where(eligible, value, np.inf)
     smallest = masked.min(axis=1)
-    tied = eligible & (score == smallest[:, None])
+    tied = eligible & (value == smallest[:, None])
     victim = np.argmin(np.where(tied, pos, np.iinfo(np.int64).max), axis=1)
     margin = np.full(G, np.inf)
-    for g in range(G):
-        e = np.sort(score[g][eligible[g]])
-        if e.size >= 2:
-            margin[g] = (e[1] - e[0]) / e[1] if e[1] > 0 else 0.0
+    if not exact:
+        for g in range(G):
+            e = np.sort(value[g][eligible[g]])
+            if e.size >= 2:
+                margin[g] = (e[1] - e[0]) / e[1] if e[1] > 0 else 0.0
     return victim, margin
 
 
@@ -147,7 +185,7 @@ class StepResult:
     evicted: np.ndarray  # [G] evicted position, -1 when nothing was evicted
     margin: np.ndarray   # [G] eviction margin (inf when nothing was evicted)
     probs: np.ndarray    # [G, n_used + 1] probabilities over the cached slots then the new token
-    slot: np.ndarray     # [G] slot the new token was written into
+    slot: np.ndarray     # [G] slot the new token was written into, -1 if it was the one evicted
 
 
 class H2OOracle:
@@ -159,9 +197,13 @@ class H2OOracle:
     token). Slots [0, n_used) are the occupied ones.
     """
 
-    def __init__(self, n_heads: int, head_dim: int, k_heavy: int, k_recent: int, scale: float):
-        if k_heavy < 0 or k_recent < 1:
-            raise ValueError("need k_heavy >= 0 and k_recent >= 1")
+    def __init__(self, n_heads: int, head_dim: int, k_heavy: int, k_recent: int, scale: float,
+                 policy: str = "accumulated"):
+        if k_heavy < 0 or k_recent < 0 or k_heavy + k_recent < 1:
+            raise ValueError("need k_heavy >= 0, k_recent >= 0 and k >= 1")
+        if policy not in POLICIES:
+            raise ValueError(f"unknown policy {policy!r}")
+        self.policy = policy
         self.G, self.d = n_heads, head_dim
         self.k_heavy, self.k_recent = k_heavy, k_recent
         self.k = k_heavy + k_recent
@@ -187,7 +229,7 @@ class H2OOracle:
         self.V[:] = 0.0
         for g in range(self.G):
             colsum[g] = prefill_column_sums(Q[g], K[g], self.scale)
-            keep, margin[g] = select_prefill(colsum[g], self.k_heavy, self.k_recent)
+            keep, margin[g] = select_prefill(colsum[g], self.k_heavy, self.k_recent, self.policy)
             m = keep.size
             self.pos[g, :m] = keep
             self.score[g, :m] = colsum[g][keep]
@@ -219,21 +261,31 @@ class H2OOracle:
 
         self.score[:, :nu] += p[:, :nu]
 
+        rows = np.arange(G)
         if nu < self.k:
             slot = np.full(G, nu, dtype=np.int64)
             evicted = np.full(G, -1, dtype=np.int64)
             margin = np.full(G, np.inf)
             self.n_used = nu + 1
         else:
-            elig = eligible_slots(self.pos, self.t, self.k_recent)
-            slot, margin = choose_victim(self.score, self.pos, elig)
-            evicted = self.pos[np.arange(G), slot].copy()
+            # Candidates: the cached slots, plus the new token itself (column k)
+            # when there is no recent window to protect it.
+            cand_pos = np.concatenate([self.pos, np.full((G, 1), self.t)], axis=1)
+            cand_score = np.concatenate([self.score, p[:, nu:nu + 1]], axis=1)
+            value = retention_value(cand_score, cand_pos, self.t, self.policy)
+            elig = eligible_slots(cand_pos, self.t, self.k_recent)
+            if self.k_recent > 0:
+                elig[:, self.k] = False
+            victim, margin = choose_victim(value, cand_pos, elig, exact=self.policy == "position")
+            evicted = cand_pos[rows, victim].copy()
+            slot = np.where(victim < self.k, victim, -1)
 
-        rows = np.arange(G)
-        self.K[rows, slot] = k_new
-        self.V[rows, slot] = v_new
-        self.pos[rows, slot] = self.t
-        self.score[rows, slot] = p[:, nu]
+        ins = slot >= 0
+        r, sl = rows[ins], slot[ins]
+        self.K[r, sl] = k_new[ins]
+        self.V[r, sl] = v_new[ins]
+        self.pos[r, sl] = self.t
+        self.score[r, sl] = p[ins, nu]
         self.t += 1
         return StepResult(out, evicted, margin, p, slot)
 

@@ -23,6 +23,7 @@ import pytest
 
 import oracle.h2o_oracle as oh
 from oracle import H2OOracle, brute_run
+from oracle.h2o_oracle import select_prefill
 from workload import Workload, make_decode, make_prompt
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -44,19 +45,19 @@ def _tiny_case(seed, n, T, d, heads=2):
     return Q, K, V, q, k, v
 
 
-def _run_oracle(Q, K, V, q, k, v, k_heavy, k_recent, scale):
+def _run_oracle(Q, K, V, q, k, v, k_heavy, k_recent, scale, policy="accumulated"):
     G, n, d = Q.shape
-    orc = H2OOracle(G, d, k_heavy, k_recent, scale)
+    orc = H2OOracle(G, d, k_heavy, k_recent, scale, policy)
     pre = orc.prefill(Q, K, V)
     kept = [set(orc.pos[g][orc.pos[g] >= 0].tolist()) for g in range(G)]
     steps = [orc.decode_step(q[:, t], k[:, t], v[:, t]) for t in range(q.shape[1])]
     return orc, pre, kept, steps
 
 
-def _compare_with_brute(Q, K, V, q, k, v, k_heavy, k_recent, scale, tol=1e-12):
-    orc, pre, kept, steps = _run_oracle(Q, K, V, q, k, v, k_heavy, k_recent, scale)
+def _compare_with_brute(Q, K, V, q, k, v, k_heavy, k_recent, scale, tol=1e-12, policy="accumulated"):
+    orc, pre, kept, steps = _run_oracle(Q, K, V, q, k, v, k_heavy, k_recent, scale, policy)
     for g in range(Q.shape[0]):
-        br = brute_run(Q[g], K[g], V[g], q[g], k[g], v[g], k_heavy, k_recent, scale)
+        br = brute_run(Q[g], K[g], V[g], q[g], k[g], v[g], k_heavy, k_recent, scale, policy)
         np.testing.assert_allclose(pre.colsum[g], br["colsum"], rtol=0, atol=tol)
         assert kept[g] == br["kept"]
         for t, st in enumerate(steps):
@@ -307,12 +308,74 @@ def test_planted_mistakes_are_caught(monkeypatch):
         "prefill_column_sums": lambda Q, K, s: orig_probs(Q, K, s).sum(axis=1),
         # recent window off by one
         "eligible_slots": lambda pos, t, kr: (pos >= 0) & (pos < t - kr),
-        # evict the largest score instead of the smallest
-        "choose_victim": lambda score, pos, e: (np.argmax(np.where(e, score, -np.inf), 1),
-                                                np.full(score.shape[0], np.inf)),
+        # evict the largest value instead of the smallest
+        "choose_victim": lambda value, pos, e, exact=False: (np.argmax(np.where(e, value, -np.inf), 1),
+                                                             np.full(value.shape[0], np.inf)),
         # heavy hitters chosen by smallest score
-        "select_prefill": lambda c, kh, kr: orig_select(-np.asarray(c) + 10, kh, kr),
+        "select_prefill": lambda c, kh, kr, policy="accumulated": orig_select(-np.asarray(c) + 10, kh, kr, policy),
     }
     for attr, fake in mutants.items():
         with monkeypatch.context() as m:
             assert _mutant_is_caught(m, attr, fake), attr
+
+
+# ----------------------------------------------------------------------------- policies
+POLICY_CASES = [
+    # (n, T, d, k_heavy, k_recent)
+    (9, 10, 8, 3, 2), (12, 8, 4, 4, 2), (6, 10, 8, 2, 1), (3, 8, 4, 2, 2),
+    (10, 9, 4, 3, 0), (8, 10, 8, 4, 0), (5, 8, 4, 1, 0), (0, 6, 4, 2, 0),
+]
+
+
+@pytest.mark.parametrize("policy", ["averaged", "position", "accumulated"])
+@pytest.mark.parametrize("case", POLICY_CASES)
+@pytest.mark.parametrize("seed", [0, 1])
+def test_policies_match_brute_force(policy, case, seed):
+    n, T, d, kh, kr = case
+    data = _tiny_case(50 * seed + n + 7, n, T, d)
+    _compare_with_brute(*data, kh, kr, 1 / math.sqrt(d), policy=policy)
+
+
+def test_position_policy_is_sink_plus_window_attention():
+    """The position policy keeps the first k_heavy tokens and the last k_recent:
+    query t attends to positions < k_heavy and to t - k_recent .. t (StreamingLLM)."""
+    G, n, T, d, sinks, w = 2, 30, 40, 8, 4, 6
+    Q, K, V, q, k, v = _tiny_case(21, n, T, d, heads=G)
+    scale = 1 / math.sqrt(d)
+    orc, _, kept, steps = _run_oracle(Q, K, V, q, k, v, sinks, w, scale, "position")
+    i = np.arange(n + T)
+    mask = (i[None, :] <= i[:, None]) & ((i[None, :] >= i[:, None] - w) | (i[None, :] < sinks))
+    for g in range(G):
+        assert kept[g] == set(range(sinks)) | set(range(n - w, n))
+        ref = _sdpa(np.concatenate([Q[g], q[g]]), np.concatenate([K[g], k[g]]),
+                    np.concatenate([V[g], v[g]]), scale, mask=mask)
+        got = np.stack([st.out[g] for st in steps])
+        np.testing.assert_allclose(got, ref[n:], rtol=0, atol=1e-12)
+        assert [int(st.evicted[g]) for st in steps] == [n + t - w for t in range(T)]
+
+
+def test_heavy_only_uniform_attention_rejects_every_new_token():
+    """k_recent = 0 with all-zero queries: older tokens always hold more
+    accumulated attention, so each new token is the one evicted and the
+    cache keeps the prompt's first k tokens."""
+    G, n, d, k, T = 2, 20, 8, 6, 15
+    rng = np.random.default_rng(4)
+    orc = H2OOracle(G, d, k, 0, 0.3)
+    orc.prefill(np.zeros((G, n, d)), rng.standard_normal((G, n, d)), rng.standard_normal((G, n, d)))
+    assert all(orc.pos[g].tolist() == list(range(k)) for g in range(G))
+    for t in range(T):
+        st = orc.decode_step(np.zeros((G, d)), rng.standard_normal((G, d)), rng.standard_normal((G, d)))
+        assert (st.evicted == n + t).all() and (st.slot == -1).all()
+        np.testing.assert_allclose(st.probs, 1.0 / (k + 1), rtol=1e-14)
+    assert all(orc.pos[g].tolist() == list(range(k)) for g in range(G))
+
+
+def test_averaged_value_counts_queries():
+    """Averaged policy: at the end of the prompt a token at j has been seen by
+    n - j queries; with uniform attention its average is (H_n - H_j) / (n - j)."""
+    n = 40
+    c = np.array([sum(1.0 / (i + 1) for i in range(j, n)) for j in range(n)])
+    keep, _ = select_prefill(c, 5, 5, "averaged")
+    avg = c[:n - 5] / (n - np.arange(n - 5))
+    expect = sorted(np.argsort(-avg, kind="stable")[:5].tolist())
+    assert keep[:5].tolist() == expect
