@@ -180,7 +180,7 @@ def main():
         """Whole path for `layers` caches: clear, prefill, T decode steps."""
         for i in layers:
             c = caches[i]
-            check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, dcode,
+            check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
                                      ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
                                      c.score.data_ptr(), c.pos.data_ptr(), sh))
             check(lib.h2o_prefill_select(ctypes.byref(c.desc), Q.data_ptr(), K.data_ptr(), V.data_ptr(), n,

@@ -51,6 +51,19 @@ typedef enum {
 
 typedef enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F16 = 2 } h2o_dtype;
 
+/*
+ * What a cached token is worth keeping (the largest values are kept at
+ * prefill, the smallest eligible one is evicted at decode; ties go by
+ * position, the later one being kept):
+ *   ACCUMULATED - its accumulated attention score (H2O, §4.1);
+ *   AVERAGED    - that score divided by the number of queries that attended
+ *                 to it, t - pos + 1 (the variant H2O §B.2 reports as worse);
+ *   POSITION    - minus its position: the first k_heavy tokens stay as
+ *                 attention sinks and the newest token outside the recent
+ *                 window leaves (StreamingLLM's sink-plus-window cache).
+ */
+typedef enum { H2O_POLICY_ACCUMULATED = 0, H2O_POLICY_AVERAGED = 1, H2O_POLICY_POSITION = 2 } h2o_policy;
+
 /* Limits of this build. */
 #define H2O_MAX_SLOTS 8192      /* k = k_heavy + k_recent */
 #define H2O_MAX_PROMPT 1048576  /* n */
@@ -74,6 +87,7 @@ typedef struct {
   int32_t batch, heads, head_dim;
   int32_t k_heavy, k_recent;
   int32_t dtype;    /* h2o_dtype */
+  int32_t policy;   /* h2o_policy */
   float scale;      /* softmax scale applied to q.k (1/sqrt(head_dim) usually) */
   void* K;
   void* V;
@@ -96,13 +110,15 @@ typedef struct {
  * Fill *cache and clear the device state: pos = -1, score = 0 for every slot
  * (K and V are left as they are), t_next = 0.
  * Requires batch, heads >= 1; head_dim in {64, 128}; k_heavy >= 0;
- * k_recent >= 1 (the recent window always holds the newest token, so a full
- * cache always has exactly one evictable slot more than k_heavy);
- * k <= H2O_MAX_SLOTS; scale finite and > 0; non-null device pointers.
+ * k_recent >= 0 with k = k_heavy + k_recent >= 1 and k <= H2O_MAX_SLOTS;
+ * policy an h2o_policy; scale finite and > 0; non-null device pointers.
+ * k_heavy = 0 is the recent-window ("Local") cache; k_recent = 0 keeps heavy
+ * hitters only (H2O §5 ablations) and lets the new token compete for a slot.
  */
 h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
-                          int32_t k_heavy, int32_t k_recent, int32_t dtype, float scale,
-                          void* K, void* V, float* score, int32_t* pos, h2o_stream_t stream);
+                          int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype,
+                          float scale, void* K, void* V, float* score, int32_t* pos,
+                          h2o_stream_t stream);
 
 /* Bytes of device workspace h2o_prefill_select needs for a prompt of n tokens. */
 size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n);
@@ -114,9 +130,10 @@ size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n);
  * For every (b,h): c_j = sum over prompt rows i >= j of softmax_j'(scale*q_i.k_j')[j]
  * (causal, own position included). If n <= k every position is kept in slots
  * 0..n-1; otherwise the recent window n-k_recent..n-1 is kept together with
- * the k_heavy positions in [0, n-k_recent) whose keys (c_j, j) are largest
- * (so equal scores keep the later position). Kept slots get K/V rows copied
- * from the prompt and score = c_j; unused slots get pos = -1, score = 0.
+ * the k_heavy positions in [0, n-k_recent) whose (value, j) are largest, the
+ * value being the policy's (c_j; c_j / (n - j); or -j), so equal values keep
+ * the later position. Kept slots get K/V rows copied from the prompt and
+ * score = c_j; unused slots get pos = -1, score = 0.
  * Afterwards t_next = n.
  *   workspace  : device buffer of at least h2o_prefill_workspace_bytes(...) bytes
  *   colsum_out : optional [batch][heads][n] fp32 device buffer receiving c, or NULL
@@ -135,10 +152,14 @@ h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, c
  * 1. p = softmax over the occupied slots plus the new token itself of scale*q.k.
  * 2. out = sum p_a V_a + p_new v_new.
  * 3. score_a += p_a for every occupied slot.
- * 4. If the cache is full (n_used == k), the victim is the slot with the
- *    smallest (score, pos) among slots with pos <= t - k_recent; exactly one
- *    slot is evicted. Otherwise nothing is evicted and the slot is n_used.
- * 5. The slot receives k_new, v_new, pos = t, score = p_new; t_next = t + 1.
+ * 4. If the cache is full (n_used == k), the victim is the candidate with the
+ *    smallest (value, pos) among slots with pos <= t - k_recent, the value
+ *    being the policy's (see h2o_policy); with k_recent = 0 the new token is
+ *    a candidate too. Exactly one token is evicted. Otherwise nothing is
+ *    evicted and the slot is n_used.
+ * 5. The freed slot receives k_new, v_new, pos = t, score = p_new, unless the
+ *    new token itself was evicted (then evicted_pos = t and no slot changes
+ *    except for the scores of step 3); t_next = t + 1.
  */
 h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,
                            float* out, int32_t* evicted_pos, h2o_stream_t stream);

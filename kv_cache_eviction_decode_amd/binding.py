@@ -24,6 +24,9 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "h2o.h")
 
 H2O_OK, H2O_EINVAL, H2O_ESTATE, H2O_EWORKSPACE, H2O_EDEVICE = 0, 1, 2, 3, 4
 H2O_F32, H2O_BF16, H2O_F16 = 0, 1, 2
+H2O_POLICY_ACCUMULATED, H2O_POLICY_AVERAGED, H2O_POLICY_POSITION = 0, 1, 2
+POLICY_CODE = {"accumulated": H2O_POLICY_ACCUMULATED, "averaged": H2O_POLICY_AVERAGED,
+               "position": H2O_POLICY_POSITION}
 DTYPE_CODE = {torch.float32: H2O_F32, torch.bfloat16: H2O_BF16, torch.float16: H2O_F16}
 CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
 STATUS_NAME = {0: "H2O_OK", 1: "H2O_EINVAL", 2: "H2O_ESTATE", 3: "H2O_EWORKSPACE", 4: "H2O_EDEVICE"}
@@ -49,7 +52,7 @@ class h2o_cache(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("k_heavy", ctypes.c_int32), ("k_recent", ctypes.c_int32), ("dtype", ctypes.c_int32),
-        ("scale", ctypes.c_float),
+        ("policy", ctypes.c_int32), ("scale", ctypes.c_float),
         ("K", ctypes.c_void_p), ("V", ctypes.c_void_p),
         ("score", ctypes.c_void_p), ("pos", ctypes.c_void_p),
         ("n_used", ctypes.c_int32), ("t_next", ctypes.c_int32),
@@ -69,7 +72,7 @@ _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _SIGNATURES = {
-    "h2o_cache_init": (_I, [ctypes.POINTER(h2o_cache), _I, _I, _I, _I, _I, _I, ctypes.c_float,
+    "h2o_cache_init": (_I, [ctypes.POINTER(h2o_cache), _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                             _P, _P, _P, _P, _P]),
     "h2o_prefill_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "h2o_prefill_select": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _I, _P, ctypes.c_size_t, _P, _P]),
@@ -139,7 +142,7 @@ def h2o_prefill_workspace_bytes(batch: int, heads: int, n: int) -> int:
     return int(load_library().h2o_prefill_workspace_bytes(batch, heads, n))
 
 
-def h2o_cache_init(desc: h2o_cache, batch, heads, head_dim, k_heavy, k_recent, scale,
+def h2o_cache_init(desc: h2o_cache, batch, heads, head_dim, k_heavy, k_recent, policy, scale,
                    K: torch.Tensor, V: torch.Tensor, score: torch.Tensor, pos: torch.Tensor, stream=None):
     k = k_heavy + k_recent
     dev = K.device
@@ -150,9 +153,10 @@ def h2o_cache_init(desc: h2o_cache, batch, heads, head_dim, k_heavy, k_recent, s
     _expect(V, "V", (batch, heads, k, head_dim), dt, dev)
     _expect(score, "score", (batch, heads, k), torch.float32, dev)
     _expect(pos, "pos", (batch, heads, k), torch.int32, dev)
+    code = POLICY_CODE.get(policy, policy) if isinstance(policy, str) else int(policy)
     _check(load_library().h2o_cache_init(ctypes.byref(desc), batch, heads, head_dim, k_heavy, k_recent,
-                                         DTYPE_CODE[dt], float(scale), _ptr(K), _ptr(V), _ptr(score),
-                                         _ptr(pos), _stream_handle(stream)))
+                                         code, DTYPE_CODE[dt], float(scale), _ptr(K), _ptr(V),
+                                         _ptr(score), _ptr(pos), _stream_handle(stream)))
 
 
 def _desc_dtype(desc):
@@ -222,7 +226,7 @@ class H2OCache:
     """One layer's H2O cache: torch-allocated device tensors plus the C descriptor."""
 
     def __init__(self, batch, heads, head_dim, k_heavy, k_recent, dtype=torch.bfloat16,
-                 scale=None, device="cuda", stream=None):
+                 scale=None, device="cuda", stream=None, policy="accumulated"):
         k = k_heavy + k_recent
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
@@ -234,7 +238,7 @@ class H2OCache:
         self.scale = float(head_dim ** -0.5 if scale is None else scale)
         self.desc = h2o_cache()
         self._workspace = None
-        h2o_cache_init(self.desc, batch, heads, head_dim, k_heavy, k_recent, self.scale,
+        h2o_cache_init(self.desc, batch, heads, head_dim, k_heavy, k_recent, policy, self.scale,
                        self.K, self.V, self.score, self.pos, stream)
 
     @property

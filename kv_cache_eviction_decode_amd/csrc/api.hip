@@ -47,15 +47,18 @@ extern "C" {
 const char* h2o_last_error(void) { return g_err; }
 
 h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
-                          int32_t k_heavy, int32_t k_recent, int32_t dtype, float scale, void* K,
-                          void* V, float* score, int32_t* pos, h2o_stream_t stream) {
+                          int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
+                          void* K, void* V, float* score, int32_t* pos, h2o_stream_t stream) {
   if (!cache) return fail(H2O_EINVAL, "cache is NULL");
   if (batch < 1 || heads < 1) return fail(H2O_EINVAL, "batch and heads must be >= 1");
   if (int64_t(batch) * heads > (int64_t(1) << 31) - 1) return fail(H2O_EINVAL, "batch*heads too large");
   if (head_dim != 64 && head_dim != 128) return fail(H2O_EINVAL, "head_dim %d not supported (64, 128)", head_dim);
   if (dtype != H2O_F32 && dtype != H2O_BF16 && dtype != H2O_F16) return fail(H2O_EINVAL, "unknown dtype %d", dtype);
   if (k_heavy < 0) return fail(H2O_EINVAL, "k_heavy must be >= 0");
-  if (k_recent < 1) return fail(H2O_EINVAL, "k_recent must be >= 1");
+  if (k_recent < 0) return fail(H2O_EINVAL, "k_recent must be >= 0");
+  if (int64_t(k_heavy) + k_recent < 1) return fail(H2O_EINVAL, "k = k_heavy + k_recent must be >= 1");
+  if (policy != H2O_POLICY_ACCUMULATED && policy != H2O_POLICY_AVERAGED && policy != H2O_POLICY_POSITION)
+    return fail(H2O_EINVAL, "unknown policy %d", policy);
   if (int64_t(k_heavy) + k_recent > H2O_MAX_SLOTS)
     return fail(H2O_EINVAL, "k = %lld exceeds %d slots", (long long)k_heavy + k_recent, H2O_MAX_SLOTS);
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(H2O_EINVAL, "scale must be finite and > 0");
@@ -70,6 +73,7 @@ h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_
   c.k_heavy = k_heavy;
   c.k_recent = k_recent;
   c.dtype = dtype;
+  c.policy = policy;
   c.scale = scale;
   c.K = K;
   c.V = V;
@@ -126,6 +130,7 @@ h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, c
   a.n = n;
   a.k_heavy = cache->k_heavy;
   a.k_recent = cache->k_recent;
+  a.policy = cache->policy;
   a.c = cache->scale * h2o::kLog2e;
   st = device_status(h2o::launch_prefill(cache->dtype, cache->head_dim, G, a, static_cast<hipStream_t>(stream)),
                      "h2o_prefill_select");
@@ -163,6 +168,7 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, c
   a.n_used = cache->n_used;
   a.t = cache->t_next;
   a.k_recent = cache->k_recent;
+  a.policy = cache->policy;
   a.c = cache->scale * h2o::kLog2e;
   st = device_status(h2o::launch_decode(cache->dtype, cache->head_dim, cache->batch * cache->heads, a,
                                         static_cast<hipStream_t>(stream)),

@@ -62,6 +62,7 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_kernel(DecodeArgs a) 
   __shared__ float sm_vnew[D];
   __shared__ uint64_t sm_key[kWaves];
   __shared__ int sm_slot[kWaves];
+  __shared__ int sm_epos[kWaves];
   extern __shared__ float sm_logit[];  // [n_used] logits in base-2 units (scored)
 
   const int head = blockIdx.x;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_kernel(DecodeArgs a) 
     float* sc_g = a.score + head_rows;
     int32_t* pos_g = a.pos + head_rows;
     uint64_t best = ~0ull;
-    int best_slot = -1;
+    int best_slot = -1, best_pos = -1;
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int slot = tid + i * kThreads;
@@ -205,10 +206,11 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_kernel(DecodeArgs a) 
         const float sc = sc_pf[i] + fast_exp2(sm_logit[slot] - M) * invZ;
         sc_g[slot] = sc;
         if (full && pos_pf[i] <= lim) {
-          const uint64_t key = score_pos_key(sc, pos_pf[i]);
+          const uint64_t key = evict_key(sc, pos_pf[i], a.t, a.policy);
           if (key < best) {
             best = key;
             best_slot = slot;
+            best_pos = pos_pf[i];
           }
         }
       }
@@ -218,11 +220,21 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_kernel(DecodeArgs a) 
       const int ps = pos_g[slot];
       sc_g[slot] = sc;
       if (full && ps <= lim) {
-        const uint64_t key = score_pos_key(sc, ps);
+        const uint64_t key = evict_key(sc, ps, a.t, a.policy);
         if (key < best) {
           best = key;
           best_slot = slot;
+          best_pos = ps;
         }
+      }
+    }
+    // Without a recent window the new token competes too (slot k = "itself").
+    if (full && a.k_recent == 0 && tid == 0) {
+      const uint64_t key = evict_key(p_new, a.t, a.t, a.policy);
+      if (key < best) {
+        best = key;
+        best_slot = a.k;
+        best_pos = a.t;
       }
     }
 
@@ -233,33 +245,38 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_kernel(DecodeArgs a) 
       for (int off = 32; off >= 1; off >>= 1) {
         const uint64_t ok = __shfl_xor(best, off);
         const int os = __shfl_xor(best_slot, off);
+        const int op = __shfl_xor(best_pos, off);
         if (ok < best) {
           best = ok;
           best_slot = os;
+          best_pos = op;
         }
       }
       if (lane == 0) {
         sm_key[wave] = best;
         sm_slot[wave] = best_slot;
+        sm_epos[wave] = best_pos;
       }
       __syncthreads();
       best = sm_key[0];
       best_slot = sm_slot[0];
+      best_pos = sm_epos[0];
 #pragma unroll
       for (int wv = 1; wv < kWaves; ++wv) {
         if (sm_key[wv] < best) {
           best = sm_key[wv];
           best_slot = sm_slot[wv];
+          best_pos = sm_epos[wv];
         }
       }
-      victim = best_slot;
-      // A full cache always has k_heavy + 1 eligible slots; if the caller's
-      // state broke that invariant nothing is written and -2 is reported.
-      evicted = victim >= 0 ? int(uint32_t(best & 0xffffffffu)) : -2;
+      // A full cache always has an eligible candidate; if the caller's state
+      // broke that invariant nothing is written and -2 is reported.
+      victim = best == ~0ull ? -1 : best_slot;
+      evicted = best == ~0ull ? -2 : best_pos;
     }
 
-    // ---- insert the new token --------------------------------------------------
-    if (victim >= 0) {
+    // ---- insert the new token (unless it was the one evicted) -----------------
+    if (victim >= 0 && victim < a.k) {
       if (tid == victim % kThreads) {  // the thread that owns the slot's score
         sc_g[victim] = p_new;
         pos_g[victim] = a.t;
@@ -273,16 +290,6 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_kernel(DecodeArgs a) 
   }
 }
 
-// ---------------------------------------------------------------------------
-// One wave per head, persistent over heads, double-buffered.
-//
-// A workgroup is a single wave that walks heads blockIdx.x, blockIdx.x +
-// gridDim.x, ... Each head is streamed in batches of UB wave-loads of K and
-// UB of V; the loads of the next batch (possibly the next head's first one)
-// are issued before the current batch is consumed, so a wave always has one
-// batch in flight, also while it merges its partials, updates the scores and
-// picks the victim of the previous head. All reductions are inside the wave
-// (DPP and lane shuffles): there is no workgroup barrier.
 template <int DT, int D, int PF>
 struct HeadInputs {
   uint4 q, kn, vn;
@@ -415,7 +422,7 @@ __global__ __launch_bounds__(64, MINW) void decode_wave_kernel(DecodeArgs a, int
       float* sc_g = a.score + hrow;
       int32_t* pos_g = a.pos + hrow;
       uint64_t best = ~0ull;
-      int best_slot = -1;
+      int best_slot = -1, best_pos = -1;
 #pragma unroll
       for (int i = 0; i < PF; ++i) {
         const int slot = lane + 64 * i;
@@ -423,10 +430,11 @@ __global__ __launch_bounds__(64, MINW) void decode_wave_kernel(DecodeArgs a, int
           const float sc = cur.sc[i] + fast_exp2(lg[i] - M) * invZ;
           sc_g[slot] = sc;
           if (full && cur.pos[i] <= lim) {
-            const uint64_t key = score_pos_key(sc, cur.pos[i]);
+            const uint64_t key = evict_key(sc, cur.pos[i], a.t, a.policy);
             if (key < best) {
               best = key;
               best_slot = slot;
+              best_pos = cur.pos[i];
             }
           }
         }
@@ -436,11 +444,21 @@ __global__ __launch_bounds__(64, MINW) void decode_wave_kernel(DecodeArgs a, int
         const int ps = pos_g[slot];
         sc_g[slot] = sc;
         if (full && ps <= lim) {
-          const uint64_t key = score_pos_key(sc, ps);
+          const uint64_t key = evict_key(sc, ps, a.t, a.policy);
           if (key < best) {
             best = key;
             best_slot = slot;
+            best_pos = ps;
           }
+        }
+      }
+      // Without a recent window the new token competes too (slot k = "itself").
+      if (full && a.k_recent == 0 && lane == 0) {
+        const uint64_t key = evict_key(p_new, a.t, a.t, a.policy);
+        if (key < best) {
+          best = key;
+          best_slot = a.k;
+          best_pos = a.t;
         }
       }
       int victim = nu;
@@ -450,14 +468,15 @@ __global__ __launch_bounds__(64, MINW) void decode_wave_kernel(DecodeArgs a, int
         // Keys are unique (positions are), so exactly one lane holds the minimum.
         const uint64_t owners = __ballot(best == gmin && gmin != ~0ull);
         if (owners) {
-          victim = __builtin_amdgcn_readlane(best_slot, __ffsll((unsigned long long)owners) - 1);
-          evicted = int(uint32_t(gmin & 0xffffffffu));
+          const int owner = __ffsll((unsigned long long)owners) - 1;
+          victim = __builtin_amdgcn_readlane(best_slot, owner);
+          evicted = __builtin_amdgcn_readlane(best_pos, owner);
         } else {
           victim = -1;  // no eligible slot: the caller's state is inconsistent
           evicted = -2;
         }
       }
-      if (victim >= 0) {
+      if (victim >= 0 && victim < a.k) {
         if (lane == victim % 64) {
           sc_g[victim] = p_new;
           pos_g[victim] = a.t;

@@ -195,4 +195,16 @@ __device__ __forceinline__ uint64_t score_pos_key(float score, int32_t pos) {
   return (uint64_t(__float_as_uint(score)) << 32) | uint32_t(pos);
 }
 
+enum : int { POLICY_ACCUMULATED = 0, POLICY_AVERAGED = 1, POLICY_POSITION = 2 };
+
+// Eviction key of a candidate at step t (the smallest leaves): its retention
+// value under the policy, then its position. Accumulated: the score; averaged:
+// the score over the t - pos + 1 queries that attended to it; position: the
+// newest token leaves first.
+__device__ __forceinline__ uint64_t evict_key(float score, int32_t pos, int32_t t, int policy) {
+  if (policy == POLICY_POSITION) return uint64_t(uint32_t(0x7FFFFFFF - pos));
+  const float v = policy == POLICY_AVERAGED ? score / float(t - pos + 1) : score;
+  return score_pos_key(v, pos);
+}
+
 }  // namespace h2o

@@ -27,6 +27,7 @@ struct DecodeArgs {
   int32_t n_used;      // occupied slots [0, n_used), or full-cache length
   int32_t t;           // position of the new token
   int32_t k_recent;
+  int32_t policy;      // h2o_policy
   float c;             // scale * log2(e)
 };
 
@@ -49,6 +50,7 @@ struct PrefillArgs {
   int32_t* cpos;
   int32_t n;
   int32_t k_heavy, k_recent;
+  int32_t policy;  // h2o_policy
   float c;         // scale * log2(e)
 };
 

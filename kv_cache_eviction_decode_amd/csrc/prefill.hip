@@ -411,9 +411,19 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int n = a.n, kh = a.k_heavy, kr = a.k_recent, k = kh + kr;
   const float* col = a.colsum + size_t(head) * n;
+  // Retention value of candidate j at the last prompt row, as float bits
+  // (monotone: values are >= 0). Accumulated: c_j; averaged: c_j / (n - j).
+  auto vbits = [&](int j) -> uint32_t {
+    const float c = col[j];
+    return __float_as_uint(a.policy == POLICY_AVERAGED ? c / float(n - j) : c);
+  };
 
   if (n <= k) {
     for (int s = tid; s < k; s += kSelThreads) slot_pos[s] = s < n ? s : -1;
+  } else if (a.policy == POLICY_POSITION) {
+    // The earliest positions are the most valuable: they are the sinks.
+    for (int s = tid; s < kh; s += kSelThreads) slot_pos[s] = s;
+    for (int s = tid; s < kr; s += kSelThreads) slot_pos[kh + s] = n - kr + s;
   } else {
     const int C = n - kr;  // heavy-hitter candidates: positions [0, C)
     uint32_t T = 0;
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
         if (tid < 256) hist[tid] = 0;
         __syncthreads();
         for (int j = tid; j < C; j += kSelThreads) {
-          const uint32_t b = __float_as_uint(col[j]);
+          const uint32_t b = vbits(j);
           if ((b & pmask) == prefix) atomicAdd(&hist[(b >> shift) & 255], 1);
         }
         __syncthreads();
@@ -448,7 +458,7 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
       int taken = 0;
       for (int base = ((C - 1) / kSelThreads) * kSelThreads; base >= 0; base -= kSelThreads) {
         const int j = base + tid;
-        const int tie = (j < C && __float_as_uint(col[j]) == T) ? 1 : 0;
+        const int tie = (j < C && vbits(j) == T) ? 1 : 0;
         int tot;
         const int below = block_exclusive_scan(tie, sm_wave, tot);
         const int above = tot - below - tie;  // ties in this chunk after j
@@ -465,7 +475,7 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
       const int j = base + tid;
       int sel = 0;
       if (kh > 0 && j < C) {
-        const uint32_t b = __float_as_uint(col[j]);
+        const uint32_t b = vbits(j);
         sel = (b > T || (b == T && j >= P)) ? 1 : 0;
       }
       int tot;

@@ -23,6 +23,7 @@ import torch
 
 from kv_cache_eviction_decode_amd import H2OCache
 from oracle import H2OOracle
+from oracle.h2o_oracle import retention_value
 from workload import Workload, make_decode, make_prompt
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -62,7 +63,7 @@ def _rel_err(got, ref):
 
 
 class ParityRun:
-    def __init__(self, wl: Workload, steps: int, sample=None, device="cuda", seed=None):
+    def __init__(self, wl: Workload, steps: int, sample=None, device="cuda", seed=None, policy="accumulated"):
         self.wl = wl
         self.steps = steps
         self.device = torch.device(device)
@@ -85,8 +86,10 @@ class ParityRun:
         self.k = to_device(kd.transpose(1, 0, 2), wl.dtype, dev).view(steps, B, H, d)
         self.v = to_device(vd.transpose(1, 0, 2), wl.dtype, dev).view(steps, B, H, d)
         del qd, kd, vd
-        self.cache = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, TORCH_DTYPE[wl.dtype], wl.scale, dev)
-        self.orc = H2OOracle(self.sample.size, d, wl.k_heavy, wl.k_recent, wl.scale)
+        self.policy = policy
+        self.cache = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, TORCH_DTYPE[wl.dtype], wl.scale, dev,
+                              policy=policy)
+        self.orc = H2OOracle(self.sample.size, d, wl.k_heavy, wl.k_recent, wl.scale, policy)
         self.report = Report()
 
     # -- views of the sampled heads on the GPU
@@ -149,10 +152,12 @@ class ParityRun:
         heavy, recent = pos[:kh], pos[kh:]
         assert recent.tolist() == list(range(n - kr, n))
         assert np.all(np.diff(heavy) > 0) and heavy.max() < n - kr
-        cand = np.ones(n - kr, bool)
-        cand[heavy] = False
-        lo_kept = colsum[heavy].min()
-        hi_dropped = colsum[: n - kr][cand].max()
+        cand = np.arange(n - kr)
+        val = retention_value(colsum[cand], cand, n - 1, self.policy)
+        dropped = np.ones(n - kr, bool)
+        dropped[heavy] = False
+        lo_kept = val[heavy].min()
+        hi_dropped = val[dropped].max()
         assert lo_kept >= hi_dropped * (1 - MARGIN), "GPU selection is not a near-tie alternative"
 
     def _check_rows(self, gpos):
@@ -213,10 +218,14 @@ class ParityRun:
         """The GPU's victim must be eligible and tie (within MARGIN) with the oracle's."""
         k = pos_before.size
         acc = score_before + st.probs[g][:k]  # accumulated scores before the insert
-        mask = pos_before == gpu_evicted
-        assert mask.sum() == 1, "GPU evicted a position that was not cached"
-        assert gpu_evicted <= tpos - self.wl.k_recent, "GPU evicted a token inside the recent window"
-        elig = pos_before <= tpos - self.wl.k_recent
-        smallest = acc[elig].min()
-        assert acc[mask][0] <= smallest * (1 + MARGIN), \
-            f"GPU victim score {acc[mask][0]} not within margin of {smallest}"
+        cand_pos = np.concatenate([pos_before, [tpos]])
+        cand_val = retention_value(np.concatenate([acc, [st.probs[g][k]]]), cand_pos, tpos, self.policy)
+        elig = cand_pos <= tpos - self.wl.k_recent
+        if self.wl.k_recent > 0:
+            elig[k] = False
+        mask = cand_pos == gpu_evicted
+        assert mask.sum() == 1, "GPU evicted a position that was not a candidate"
+        assert elig[mask][0], "GPU evicted a token inside the recent window"
+        smallest = cand_val[elig].min()
+        assert cand_val[mask][0] <= smallest + abs(smallest) * MARGIN, \
+            f"GPU victim value {cand_val[mask][0]} not within margin of {smallest}"

@@ -35,21 +35,24 @@ def test_workspace_bytes():
 
 
 def test_struct_layout_matches_header():
-    # the descriptor is a plain C struct: 7 x 4-byte fields, 4 pointers, 2 int32, int64, 2 uint32
-    assert ctypes.sizeof(b.h2o_cache) == 7 * 4 + 4 + 4 * 8 + 2 * 4 + 8 + 2 * 4
+    # the descriptor is a plain C struct: 8 x 4-byte fields, 4 pointers, 2 int32, int64, 2 uint32
+    assert ctypes.sizeof(b.h2o_cache) == 8 * 4 + 4 * 8 + 2 * 4 + 8 + 2 * 4
     assert b.h2o_cache.K.offset == 32 and b.h2o_cache.steps.offset == 72
     assert ctypes.sizeof(b.h2o_state) == 32
 
 
 @pytest.mark.parametrize("args,msg", [
-    ((1, 1, 96, 1, 1, 1, 0.1), "head_dim"),
-    ((1, 1, 128, 1, 0, 1, 0.1), "k_recent"),
-    ((1, 1, 128, -1, 1, 1, 0.1), "k_heavy"),
-    ((0, 1, 128, 1, 1, 1, 0.1), "batch"),
-    ((1, 1, 128, 8192, 1, 1, 0.1), "exceeds"),
-    ((1, 1, 128, 1, 1, 7, 0.1), "dtype"),
-    ((1, 1, 128, 1, 1, 1, float("nan")), "scale"),
-    ((1, 1, 128, 1, 1, 1, 0.1), "non-NULL"),
+    ((1, 1, 96, 1, 1, 0, 1, 0.1), "head_dim"),
+    ((1, 1, 128, 1, -1, 0, 1, 0.1), "k_recent"),
+    ((1, 1, 128, 0, 0, 0, 1, 0.1), "k = k_heavy + k_recent must be >= 1"),
+    ((1, 1, 128, -1, 1, 0, 1, 0.1), "k_heavy"),
+    ((0, 1, 128, 1, 1, 0, 1, 0.1), "batch"),
+    ((1, 1, 128, 8192, 1, 0, 1, 0.1), "exceeds"),
+    ((1, 1, 128, 1, 1, 0, 7, 0.1), "dtype"),
+    ((1, 1, 128, 1, 1, 3, 1, 0.1), "policy"),
+    ((1, 1, 128, 1, 1, 0, 1, float("nan")), "scale"),
+    ((1, 1, 128, 1, 1, 0, 1, 0.1), "non-NULL"),
+    ((1, 1, 128, 4, 0, 2, 1, 0.1), "non-NULL"),
 ])
 def test_init_rejects_bad_arguments_without_launching(args, msg):
     lib = b.load_library()

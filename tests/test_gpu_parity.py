@@ -43,6 +43,39 @@ def test_small_parity(gpu, case):
     assert rep.steps == T
 
 
+POLICY_CASES = [
+    # name, policy, B, H, d, dtype, n, k_heavy, k_recent, T
+    ("averaged_bf16", "averaged", 2, 3, 128, "bf16", 300, 20, 20, 50),
+    ("averaged_f32_d64", "averaged", 1, 2, 64, "f32", 129, 9, 7, 40),
+    ("position_bf16", "position", 2, 2, 128, "bf16", 333, 4, 28, 40),
+    ("position_f16_fill", "position", 1, 3, 64, "f16", 10, 4, 12, 30),
+    ("heavy_only_bf16", "accumulated", 2, 3, 128, "bf16", 300, 32, 0, 50),
+    ("heavy_only_averaged_f16", "averaged", 1, 2, 128, "f16", 200, 24, 0, 40),
+    ("heavy_only_fill_f32", "accumulated", 1, 2, 64, "f32", 5, 12, 0, 30),
+]
+
+
+@pytest.mark.parametrize("case", POLICY_CASES, ids=[c[0] for c in POLICY_CASES])
+def test_policy_parity(gpu, case):
+    name, policy, B, H, d, dt, n, kh, kr, T = case
+    wl = Workload(name, B, H, d, dt, n, kh, kr, T, 1.5, 0.0, seed=zlib.crc32(name.encode()) % 10000)
+    run = ParityRun(wl, T, policy=policy)
+    run.prefill()
+    rep = run.decode()
+    log(f"[parity] {name} ({policy}): {rep}")
+    assert rep.steps == T
+
+
+def test_policy_full_size_sampled(gpu):
+    """The averaged and heavy-only variants at the OPT-6.7B layer shape (same grid as the bench)."""
+    for policy, kh, kr in (("averaged", 128, 128), ("accumulated", 256, 0)):
+        wl = WORKLOADS["opt6.7b_layer"].with_(k_heavy=kh, k_recent=kr)
+        run = ParityRun(wl, 48, sample=sample_heads(wl, 16), policy=policy)
+        run.prefill()
+        rep = run.decode()
+        log(f"[parity] opt6.7b_layer {policy} k_heavy={kh} k_recent={kr}: {rep}")
+
+
 def test_tiny_f32_workload_full(gpu):
     wl = WORKLOADS["tiny_f32"]
     run = ParityRun(wl, wl.steps)
