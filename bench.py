@@ -31,7 +31,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
 METRIC = "H2O decode head-steps/sec + achieved HBM GB/s (% of MI355X peak)"
-DECODE_SOURCES = ["decode.hip", "h2o_device.h", "launch.h"]
+DECODE_SOURCES = {"fused": ["decode.hip", "h2o_device.h", "launch.h"],
+                  "split": ["decode_split.hip", "h2o_device.h", "launch.h"]}
 
 
 def log(*a):
@@ -47,6 +48,11 @@ def parse_args():
     p.add_argument("--layers", type=int, default=4, help="independent layer caches decoded in rotation")
     p.add_argument("--decode-steps", type=int, default=None,
                    help="decode steps per bench step (default: the workload's own count; for profiling runs)")
+    p.add_argument("--batch", type=int, default=None, help="override the workload's batch")
+    p.add_argument("--heads", type=int, default=None, help="override the workload's heads")
+    p.add_argument("--decode", choices=("fused", "split"), default="fused",
+                   help="decode entry point: h2o_decode_step (fused) or h2o_decode_step_split")
+    p.add_argument("--chunk-rows", type=int, default=0, help="split decode chunk length (0 = library's choice)")
     p.add_argument("--cpu-heads", type=int, default=256, help="heads in the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-single-layer", action="store_true")
@@ -55,9 +61,9 @@ def parse_args():
     return p.parse_args()
 
 
-def decode_source_digest() -> str:
+def decode_source_digest(mode: str = "fused") -> str:
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in DECODE_SOURCES[mode]:
         with open(os.path.join(ROOT, "kv_cache_eviction_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -73,8 +79,9 @@ def decode_bytes_per_head(n_used: int, d: int, e: int) -> int:
     return 2 * n_used * d * e + 12 * n_used + 5 * d * e + 4 * d + 8
 
 
-def load_traffic(workload: str, digest: str):
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.json")
+def load_traffic(workload: str, digest: str, mode: str = "fused"):
+    name = f"decode_{workload}" if mode == "fused" else f"decode_split_{workload}"
+    path = os.path.join(ROOT, "profiles", f"{name}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -135,6 +142,8 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.decode_steps is not None:
         wl = wl.with_(steps=max(1, min(args.decode_steps, wl.steps)))
+    if args.batch is not None or args.heads is not None:
+        wl = wl.with_(batch=args.batch or wl.batch, heads=args.heads or wl.heads)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
@@ -171,6 +180,8 @@ def main():
     kp = [ks[t].data_ptr() for t in range(T)]
     vp = [vs[t].data_ptr() for t in range(T)]
     dcode = {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype]
+    split = args.decode == "split"
+    sws = caches[0].split_workspace() if split else None  # shared: calls are serialised on one stream
 
     def check(st):
         if st != 0:
@@ -189,8 +200,13 @@ def main():
             ev.record(stream)
         for t in range(T):
             for i in layers:
-                check(lib.h2o_decode_step(ctypes.byref(caches[i].desc), qp[t], kp[t], vp[t],
-                                          outs[i].data_ptr(), evs[i].data_ptr(), sh))
+                if split:
+                    check(lib.h2o_decode_step_split(ctypes.byref(caches[i].desc), qp[t], kp[t], vp[t],
+                                                    outs[i].data_ptr(), evs[i].data_ptr(), args.chunk_rows,
+                                                    sws.data_ptr(), sws.numel(), sh))
+                else:
+                    check(lib.h2o_decode_step(ctypes.byref(caches[i].desc), qp[t], kp[t], vp[t],
+                                              outs[i].data_ptr(), evs[i].data_ptr(), sh))
 
     all_layers = list(range(L))
     for _ in range(args.warmup):
@@ -220,8 +236,8 @@ def main():
     launches = T * L
     avg_launch_s = (sum(decode_ms) / args.steps) / 1e3 / launches
     achieved = bytes_per_launch / avg_launch_s / 1e9
-    digest = decode_source_digest()
-    traffic = load_traffic(wl.name, digest)
+    digest = decode_source_digest(args.decode)
+    traffic = load_traffic(wl.name, digest, args.decode) if args.batch is None and args.heads is None else None
     prefill_flops = 2.0 * n * (n + 1) * d * G  # two causal QK^T passes per layer
     pf_s = (sum(prefill_ms) / args.steps) / 1e3 / L
 
@@ -238,7 +254,8 @@ def main():
         dms = e1[1].elapsed_time(e2)
         single = {"decode_us_per_launch": dms * 1e3 / T,
                   "decode_GBps": bytes_per_launch / (dms / 1e3 / T) / 1e9,
-                  "note": "one cache decoded alone: its 268 MB are partly re-read from the 256 MB Infinity Cache"}
+                  "note": f"one cache decoded alone: its {bytes_per_launch / 1e6:.0f} MB per step can be partly "
+                          "re-read from the 256 MB Infinity Cache"}
 
     result = {
         "metric": METRIC,
@@ -255,10 +272,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "heads": H, "head_dim": d, "prompt_len": n,
                    "k_heavy": wl.k_heavy, "k_recent": wl.k_recent, "decode_steps": T, "layers": L,
-                   "pareto_alpha": wl.alpha, "parallelism": "none (1 GPU)"},
+                   "pareto_alpha": wl.alpha, "parallelism": "none (1 GPU)", "decode_entry": args.decode},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "h2o decode_kernel (fused attention + score + evict + insert)",
+                     "kernel": ("h2o decode_split_kernel (chunked attention, last chunk merges + scores + "
+                                "evicts + inserts)" if split else
+                                "h2o decode_kernel (fused attention + score + evict + insert)"),
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
                      "kernel_source_digest": digest},
         "decode_head_steps_per_s": head_steps / (sum(decode_ms) / args.steps / 1e3),

@@ -165,6 +165,35 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, c
                            float* out, int32_t* evicted_pos, h2o_stream_t stream);
 
 /*
+ * Bytes of device workspace h2o_decode_step_split needs for a cache of
+ * batch x heads heads, head_dim and k = k_heavy + k_recent slots (0 for an
+ * invalid shape). The workspace holds the step's logits [batch][heads][k] and
+ * up to ceil(k/64) chunk partials per head; it carries nothing from one call
+ * to the next.
+ */
+size_t h2o_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t k);
+
+/*
+ * The decode step of h2o_decode_step, same arguments, same results (up to the
+ * fp32 summation order of the softmax), with every head's occupied slots cut
+ * into chunks of chunk_rows rows, each streamed by its own wave, so that few
+ * (batch, head) pairs with long caches still fill the GPU. A second kernel
+ * merges the chunks' partial softmax sums per head (H2O §D "Recursive
+ * attention"), updates the scores and evicts (H2O §2 "Problem formulation",
+ * §D "Cache eviction").
+ *   chunk_rows : 0 lets the library choose (about two waves per SIMD in
+ *                total); otherwise a positive multiple of 64
+ *   workspace  : device buffer of at least h2o_decode_workspace_bytes(...)
+ *                bytes, 256-byte aligned, used only while the call's work
+ *                runs on the stream (calls sharing one workspace must be
+ *                issued in order on one stream).
+ * For many heads with short caches h2o_decode_step is the faster call.
+ */
+h2o_status h2o_decode_step_split(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                 float* out, int32_t* evicted_pos, int32_t chunk_rows, void* workspace,
+                                 size_t workspace_bytes, h2o_stream_t stream);
+
+/*
  * Export the cache state (checkpoint, inspection). Fills *state from the host
  * counters. If pos_host and/or score_host are non-null ([batch][heads][k]
  * host arrays), the device arrays are copied into them and the call waits for

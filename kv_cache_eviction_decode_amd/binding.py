@@ -77,6 +77,8 @@ _SIGNATURES = {
     "h2o_prefill_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "h2o_prefill_select": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _I, _P, ctypes.c_size_t, _P, _P]),
     "h2o_decode_step": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _P, _P, _P]),
+    "h2o_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "h2o_decode_step_split": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
     "h2o_cache_state": (_I, [ctypes.POINTER(h2o_cache), ctypes.POINTER(h2o_state), _P, _P, _P]),
     "h2o_cache_restore": (_I, [ctypes.POINTER(h2o_cache), _I, ctypes.c_int64]),
     "h2o_fullcache_decode": (_I, [_I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P, _P, _P]),
@@ -191,6 +193,24 @@ def h2o_decode_step(desc: h2o_cache, q, k_new, v_new, out, evicted, stream=None,
                                           _ptr(out), _ptr(evicted), _stream_handle(stream)))
 
 
+def h2o_decode_workspace_bytes(batch: int, heads: int, head_dim: int, k: int) -> int:
+    return int(load_library().h2o_decode_workspace_bytes(batch, heads, head_dim, k))
+
+
+def h2o_decode_step_split(desc: h2o_cache, q, k_new, v_new, out, evicted, workspace: torch.Tensor,
+                          chunk_rows: int = 0, stream=None, device=None):
+    B, H, d = desc.batch, desc.heads, desc.head_dim
+    dt = _desc_dtype(desc)
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
+        _expect(t, name, (B, H, d), dt, device)
+    _expect(out, "out", (B, H, d), torch.float32, device)
+    _expect(evicted, "evicted", (B, H), torch.int32, device)
+    _expect(workspace, "workspace", (workspace.numel(),), torch.uint8, device)
+    _check(load_library().h2o_decode_step_split(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                                _ptr(out), _ptr(evicted), int(chunk_rows), _ptr(workspace),
+                                                workspace.numel(), _stream_handle(stream)))
+
+
 def h2o_cache_state(desc: h2o_cache, pos_host=None, score_host=None, stream=None) -> h2o_state:
     st = h2o_state()
     k = desc.k_heavy + desc.k_recent
@@ -238,6 +258,7 @@ class H2OCache:
         self.scale = float(head_dim ** -0.5 if scale is None else scale)
         self.desc = h2o_cache()
         self._workspace = None
+        self._split_ws = None
         h2o_cache_init(self.desc, batch, heads, head_dim, k_heavy, k_recent, policy, self.scale,
                        self.K, self.V, self.score, self.pos, stream)
 
@@ -278,6 +299,22 @@ class H2OCache:
         if evicted is None:
             evicted = torch.empty(self.batch, self.heads, dtype=torch.int32, device=self.device)
         h2o_decode_step(self.desc, q, k_new, v_new, out, evicted, stream, self.device)
+        return out, evicted
+
+    def split_workspace(self) -> torch.Tensor:
+        """Workspace of the split decode step (logits and per-chunk partials)."""
+        if self._split_ws is None:
+            need = h2o_decode_workspace_bytes(self.batch, self.heads, self.desc.head_dim, self.k)
+            self._split_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._split_ws
+
+    def decode_step_split(self, q, k_new, v_new, out=None, evicted=None, chunk_rows=0, stream=None):
+        if out is None:
+            out = torch.empty(self.batch, self.heads, self.desc.head_dim, dtype=torch.float32, device=self.device)
+        if evicted is None:
+            evicted = torch.empty(self.batch, self.heads, dtype=torch.int32, device=self.device)
+        h2o_decode_step_split(self.desc, q, k_new, v_new, out, evicted, self.split_workspace(), chunk_rows,
+                              stream, self.device)
         return out, evicted
 
     def state(self, copy=False, stream=None):

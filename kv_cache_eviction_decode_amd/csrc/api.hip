@@ -40,6 +40,12 @@ h2o_status check_cache(const h2o_cache* c) {
 size_t lse_ld(int32_t n) { return (size_t(n) + 63) & ~size_t(63); }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Split decode: chunks are whole multiples of 64 rows, so a head has at most
+// ceil(k / 64) of them.
+constexpr int kSplitRows = 64;
+size_t split_cmax(int32_t k) { return (size_t(k) + kSplitRows - 1) / kSplitRows; }
+static_assert((H2O_MAX_SLOTS + kSplitRows - 1) / kSplitRows <= h2o::kMaxChunks, "split chunk capacity");
+
 }  // namespace
 
 extern "C" {
@@ -147,8 +153,8 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, c
   if (st != H2O_OK) return st;
   if (!q || !k_new || !v_new || !out || !evicted_pos)
     return fail(H2O_EINVAL, "q, k_new, v_new, out and evicted_pos must be non-NULL");
-  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 4) || !aligned(evicted_pos, 4))
-    return fail(H2O_EINVAL, "q, k_new, v_new must be 16-byte aligned; out, evicted_pos 4-byte aligned");
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) || !aligned(evicted_pos, 4))
+    return fail(H2O_EINVAL, "q, k_new, v_new, out must be 16-byte aligned; evicted_pos 4-byte aligned");
   if (cache->t_next == INT32_MAX) return fail(H2O_ESTATE, "position counter exhausted");
 
   const int32_t k = cache->k_heavy + cache->k_recent;
@@ -173,6 +179,82 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, c
   st = device_status(h2o::launch_decode(cache->dtype, cache->head_dim, cache->batch * cache->heads, a,
                                         static_cast<hipStream_t>(stream)),
                      "h2o_decode_step");
+  if (st != H2O_OK) return st;
+  cache->t_next += 1;
+  cache->n_used = cache->n_used < k ? cache->n_used + 1 : k;
+  cache->steps += 1;
+  return H2O_OK;
+}
+
+size_t h2o_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t k) {
+  if (batch < 1 || heads < 1 || k < 1 || k > H2O_MAX_SLOTS || (head_dim != 64 && head_dim != 128)) return 0;
+  const size_t G = size_t(batch) * heads;
+  const size_t cmax = split_cmax(k);
+  return align256(G * k * sizeof(float)) + align256(G * cmax * 2 * sizeof(float)) +
+         align256(G * cmax * head_dim * sizeof(float));
+}
+
+h2o_status h2o_decode_step_split(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                 float* out, int32_t* evicted_pos, int32_t chunk_rows, void* workspace,
+                                 size_t workspace_bytes, h2o_stream_t stream) {
+  h2o_status st = check_cache(cache);
+  if (st != H2O_OK) return st;
+  if (!q || !k_new || !v_new || !out || !evicted_pos)
+    return fail(H2O_EINVAL, "q, k_new, v_new, out and evicted_pos must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) || !aligned(evicted_pos, 4))
+    return fail(H2O_EINVAL, "q, k_new, v_new, out must be 16-byte aligned; evicted_pos 4-byte aligned");
+  if (chunk_rows < 0 || chunk_rows % kSplitRows != 0)
+    return fail(H2O_EINVAL, "chunk_rows must be 0 or a positive multiple of %d", kSplitRows);
+  const int32_t k = cache->k_heavy + cache->k_recent;
+  const size_t need = h2o_decode_workspace_bytes(cache->batch, cache->heads, cache->head_dim, k);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(H2O_EWORKSPACE, "split decode needs a 256-byte aligned workspace of %zu bytes", need);
+  if (cache->t_next == INT32_MAX) return fail(H2O_ESTATE, "position counter exhausted");
+
+  const int G = cache->batch * cache->heads;
+  const int nu = cache->n_used;
+  int L = chunk_rows;
+  if (L == 0) {
+    // About two waves per SIMD in total, at least one 64-row chunk each.
+    const int64_t target = int64_t(h2o::cu_count()) * 4 * 2;
+    const int64_t per = (int64_t(G) * nu + target - 1) / target;
+    L = int(((per + kSplitRows - 1) / kSplitRows) * kSplitRows);
+    if (L < kSplitRows) L = kSplitRows;
+  }
+  const int chunks = nu > 0 ? (nu + L - 1) / L : 1;
+  if (chunks > split_cmax(k)) return fail(H2O_EINVAL, "chunk_rows %d too small for k = %d", L, k);
+
+  h2o::DecodeArgs a{};
+  a.K = cache->K;
+  a.V = cache->V;
+  a.K_w = cache->K;
+  a.V_w = cache->V;
+  a.score = cache->score;
+  a.pos = cache->pos;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.out = out;
+  a.evicted = evicted_pos;
+  a.k = k;
+  a.n_used = nu;
+  a.t = cache->t_next;
+  a.k_recent = cache->k_recent;
+  a.policy = cache->policy;
+  a.c = cache->scale * h2o::kLog2e;
+  char* ws = static_cast<char*>(workspace);
+  const size_t cmax = split_cmax(k);
+  h2o::SplitArgs w{};
+  w.logit = reinterpret_cast<float*>(ws);
+  ws += align256(size_t(G) * k * sizeof(float));
+  w.part_ml = reinterpret_cast<float*>(ws);
+  ws += align256(size_t(G) * cmax * 2 * sizeof(float));
+  w.part_acc = reinterpret_cast<float*>(ws);
+  w.chunk_len = L;
+  w.chunks = chunks;
+  w.cmax = int(cmax);
+  st = device_status(h2o::launch_decode_split(cache->dtype, cache->head_dim, G, a, w, static_cast<hipStream_t>(stream)),
+                     "h2o_decode_step_split");
   if (st != H2O_OK) return st;
   cache->t_next += 1;
   cache->n_used = cache->n_used < k ? cache->n_used + 1 : k;
@@ -234,8 +316,8 @@ h2o_status h2o_fullcache_decode(int32_t batch, int32_t heads, int32_t head_dim, 
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(H2O_EINVAL, "scale must be finite and > 0");
   if (len < 1) return fail(H2O_EINVAL, "len must be >= 1");
   if (!q || !Kc || !Vc || !out) return fail(H2O_EINVAL, "q, K, V and out must be non-NULL");
-  if (!aligned(q, 16) || !aligned(Kc, 16) || !aligned(Vc, 16) || !aligned(out, 4))
-    return fail(H2O_EINVAL, "q, K, V must be 16-byte aligned; out 4-byte aligned");
+  if (!aligned(q, 16) || !aligned(Kc, 16) || !aligned(Vc, 16) || !aligned(out, 16))
+    return fail(H2O_EINVAL, "q, K, V and out must be 16-byte aligned");
   h2o::DecodeArgs a{};
   a.K = Kc;
   a.V = Vc;

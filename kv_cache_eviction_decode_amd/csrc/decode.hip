@@ -34,17 +34,6 @@
 namespace h2o {
 namespace {
 
-template <int DT, int D, int WAVES>
-struct Shape {
-  static constexpr int E = Elem<DT>::bytes;
-  static constexpr int ROW = D * E;      // bytes per cache row
-  static constexpr int LPR = ROW / 16;   // lanes per row
-  static constexpr int RPU = 64 / LPR;   // rows per wave-wide load
-  static constexpr int EPL = 16 / E;     // elements per lane
-  static constexpr int NP = WAVES * RPU;  // online-softmax partials per workgroup
-  static_assert(LPR >= 4 && LPR <= 64, "row must span 4..64 lanes");
-};
-
 // SCORED = true: the H2O step. SCORED = false: plain attention over a
 // contiguous cache of n_used rows (no new token, no scores, no eviction).
 //   WAVES: waves per workgroup (the head's rows are split over them)
@@ -518,18 +507,6 @@ __global__ __launch_bounds__(64, MINW) void decode_wave_kernel(DecodeArgs a, int
   }
 }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
-  }
-  return n;
-}
 
 template <int DT, int D, bool SCORED>
 hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
@@ -564,6 +541,19 @@ hipError_t dispatch(int dtype, int head_dim, int G, const DecodeArgs& a, hipStre
 }
 
 }  // namespace
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
 
 hipError_t launch_decode(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s) {
   return dispatch<true>(dtype, head_dim, G, a, s);

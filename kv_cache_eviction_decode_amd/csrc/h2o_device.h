@@ -90,6 +90,19 @@ template <> struct Unpack<DT_F32> {
   }
 };
 
+// Rows of d elements streamed with 16-byte loads: a row is read by LPR = d*bytes/16
+// consecutive lanes, so one wave-wide load covers RPU = 64/LPR consecutive rows.
+template <int DT, int D, int WAVES>
+struct Shape {
+  static constexpr int E = Elem<DT>::bytes;
+  static constexpr int ROW = D * E;      // bytes per cache row
+  static constexpr int LPR = ROW / 16;   // lanes per row
+  static constexpr int RPU = 64 / LPR;   // rows per wave-wide load
+  static constexpr int EPL = 16 / E;     // elements per lane
+  static constexpr int NP = WAVES * RPU;  // online-softmax partials per workgroup
+  static_assert(LPR >= 4 && LPR <= 64, "row must span 4..64 lanes");
+};
+
 // DPP lane permutations inside a 16-lane row.
 template <int CTRL> __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(

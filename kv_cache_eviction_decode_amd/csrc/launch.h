@@ -31,9 +31,29 @@ struct DecodeArgs {
   float c;             // scale * log2(e)
 };
 
+// Compute units of the current device (256 on MI355X).
+int cu_count();
+
 // Fused H2O decode step: attention over n_used slots + the new token, score
 // accumulation, at most one eviction, insert. One workgroup per head.
 hipError_t launch_decode(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);
+
+// Split decode: the occupied slots of every head are cut into `chunks` runs of
+// `chunk_len` rows (the last one ragged), each streamed by its own wave; a
+// second kernel merges them per head.
+struct SplitArgs {
+  float* logit;       // [G][k] logits of the step, base-2 units
+  float* part_ml;     // [G][cmax][2] per-chunk (max, sum) of the online softmax
+  float* part_acc;    // [G][cmax][d] per-chunk unnormalised P.V
+  int32_t chunk_len;  // rows per chunk, a multiple of 64
+  int32_t chunks;     // ceil(n_used / chunk_len), at least 1
+  int32_t cmax;       // chunk capacity per head in the workspace
+};
+// Chunks of at least 64 rows over at most 8192 slots.
+constexpr int kMaxChunks = 128;
+
+hipError_t launch_decode_split(int dtype, int head_dim, int G, const DecodeArgs& a, const SplitArgs& s,
+                               hipStream_t st);
 
 // Plain attention of one query over a contiguous cache of n_used rows.
 hipError_t launch_fullcache(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);

@@ -63,15 +63,20 @@ def _rel_err(got, ref):
 
 
 class ParityRun:
-    def __init__(self, wl: Workload, steps: int, sample=None, device="cuda", seed=None, policy="accumulated"):
+    def __init__(self, wl: Workload, steps: int, sample=None, device="cuda", seed=None, policy="accumulated",
+                 split_rows=None):
+        """split_rows: None decodes with h2o_decode_step; an int (0 = the library's
+        choice) decodes with h2o_decode_step_split in chunks of that many rows."""
         self.wl = wl
+        self.split_rows = split_rows
         self.steps = steps
         self.device = torch.device(device)
         G = wl.n_heads_total
         self.sample = np.arange(G) if sample is None else np.asarray(sample)
         self.sample_t = torch.from_numpy(self.sample).to(self.device)
         B, H, n, d = wl.batch, wl.heads, wl.prompt_len, wl.head_dim
-        log(f"[parity] {wl.describe()} steps={steps} sampled_heads={self.sample.size}")
+        mode = "fused" if split_rows is None else f"split(chunk_rows={split_rows})"
+        log(f"[parity] {wl.describe()} steps={steps} sampled_heads={self.sample.size} decode={mode}")
         Q, K, V = make_prompt(wl, seed=seed)
         qd, kd, vd = make_decode(wl, steps=steps, seed=seed)
         self.oQ, self.oK, self.oV = Q[self.sample], K[self.sample], V[self.sample]
@@ -184,7 +189,10 @@ class ParityRun:
             pos_before = self.orc.pos.copy()
             score_before = self.orc.score.copy()
             tpos = self.orc.t
-            self.cache.decode_step(self.q[t], self.k[t], self.v[t], out, ev)
+            if self.split_rows is None:
+                self.cache.decode_step(self.q[t], self.k[t], self.v[t], out, ev)
+            else:
+                self.cache.decode_step_split(self.q[t], self.k[t], self.v[t], out, ev, self.split_rows)
             st = self.orc.decode_step(self.oq[:, t], self.ok[:, t], self.ov[:, t])
             gout = self._gpu_sampled(out)
             gev = self._gpu_sampled(ev)

@@ -34,6 +34,15 @@ def test_workspace_bytes():
     assert ws(8, 32, 16384) == 2 * 8 * 32 * 16384 * 4
 
 
+def test_decode_workspace_bytes():
+    ws = b.h2o_decode_workspace_bytes
+    # logits [k], ceil(k/64) partials of (max, sum) and d accumulators, 256-byte aligned regions
+    assert ws(1, 1, 128, 2048) == 8192 + 256 + 32 * 128 * 4
+    assert ws(8, 32, 128, 2048) == 256 * 2048 * 4 + 256 * 32 * 2 * 4 + 256 * 32 * 128 * 4
+    assert ws(1, 1, 64, 65) == 512 + 256 + 512
+    assert ws(1, 1, 96, 64) == 0 and ws(1, 1, 128, 0) == 0 and ws(1, 1, 128, 8193) == 0
+
+
 def test_struct_layout_matches_header():
     # the descriptor is a plain C struct: 8 x 4-byte fields, 4 pointers, 2 int32, int64, 2 uint32
     assert ctypes.sizeof(b.h2o_cache) == 8 * 4 + 4 * 8 + 2 * 4 + 8 + 2 * 4
@@ -71,6 +80,7 @@ def test_calls_on_uninitialised_cache_are_rejected():
     assert lib.h2o_prefill_select(ctypes.byref(d), None, None, None, 4, None, 0, None, None) == b.H2O_ESTATE
     assert lib.h2o_cache_state(ctypes.byref(d), ctypes.byref(st_), None, None, None) == b.H2O_ESTATE
     assert lib.h2o_cache_restore(ctypes.byref(d), 3, 0) == b.H2O_ESTATE
+    assert lib.h2o_decode_step_split(ctypes.byref(d), None, None, None, None, None, 0, None, 0, None) == b.H2O_ESTATE
     assert lib.h2o_decode_step(None, None, None, None, None, None, None) == b.H2O_EINVAL
 
 

@@ -1,0 +1,80 @@
+"""GPU parity of the split decode entry point (h2o_decode_step_split) against
+the fp64 oracle, through the C ABI.
+
+Chunk lengths are chosen so that heads have one chunk, a few, a ragged last
+chunk, more than 64 chunks (the merge loops over lane-sized groups of
+partials) and an empty chunk (empty cache). The cache grows through chunk
+boundaries while it fills. The named long-context workload runs at its full
+shape with the library's own chunking, as in the benchmark, and so does a
+few-heads shape (one sequence of eight heads).
+"""
+import zlib
+
+import pytest
+import torch
+
+from h2o_harness import ParityRun, log
+from workload import WORKLOADS, Workload, sample_heads
+
+pytestmark = pytest.mark.gpu
+
+SPLIT_CASES = [
+    # name, policy, B, H, d, dtype, n, k_heavy, k_recent, T, chunk_rows
+    ("ragged_chunks_bf16", "accumulated", 1, 3, 128, "bf16", 700, 150, 150, 30, 64),
+    ("fills_across_chunks_f16_d64", "accumulated", 1, 2, 64, "f16", 100, 100, 100, 120, 64),
+    ("auto_chunks_f32", "accumulated", 2, 2, 128, "f32", 900, 200, 100, 20, 0),
+    ("one_chunk_bf16", "accumulated", 2, 2, 128, "bf16", 300, 40, 40, 30, 128),
+    ("empty_prompt_bf16", "accumulated", 1, 2, 128, "bf16", 0, 40, 40, 100, 64),
+    ("heavy_only_bf16", "accumulated", 1, 2, 128, "bf16", 500, 256, 0, 30, 128),
+    ("averaged_bf16_d64", "averaged", 1, 2, 64, "bf16", 600, 128, 64, 30, 64),
+    ("position_f16", "position", 1, 2, 128, "f16", 400, 8, 120, 30, 64),
+    ("many_chunks_bf16", "accumulated", 1, 1, 128, "bf16", 9000, 4096, 4096, 4, 64),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_parity(gpu, case):
+    name, policy, B, H, d, dt, n, kh, kr, T, rows = case
+    wl = Workload(name, B, H, d, dt, n, kh, kr, T, 1.5, 0.0, seed=zlib.crc32(name.encode()) % 10000)
+    run = ParityRun(wl, T, policy=policy, split_rows=rows)
+    run.prefill()
+    rep = run.decode()
+    log(f"[split] {name} ({policy}, chunk_rows={rows}): {rep}")
+    assert rep.steps == T
+
+
+def test_split_long_context_full_size(gpu):
+    """The long-context layer (256 heads x 2048 slots) with the library's chunking."""
+    wl = WORKLOADS["long_context"]
+    run = ParityRun(wl, 24, sample=sample_heads(wl, 4), split_rows=0)
+    run.prefill()
+    rep = run.decode()
+    log(f"[split] long_context full size: {rep}")
+    assert rep.steps == 24
+
+
+def test_split_few_heads_auto_chunks(gpu):
+    """Eight heads of 2048 slots: the library cuts each into 32 chunks."""
+    wl = WORKLOADS["long_context"].with_(batch=1, heads=8, prompt_len=4096, steps=40)
+    run = ParityRun(wl, wl.steps, split_rows=0)
+    run.prefill()
+    rep = run.decode()
+    log(f"[split] few heads: {rep}")
+    assert rep.steps == wl.steps
+
+
+def test_split_errors(gpu):
+    from kv_cache_eviction_decode_amd import H2OCache, binding as b
+    c = H2OCache(1, 2, 128, 8, 8, torch.bfloat16, device="cuda")
+    q = torch.zeros(1, 2, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(1, 2, 128, dtype=torch.float32, device="cuda")
+    ev = torch.empty(1, 2, dtype=torch.int32, device="cuda")
+    small = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(b.H2OError, match="H2O_EWORKSPACE"):
+        b.h2o_decode_step_split(c.desc, q, q, q, out, ev, small, 0)
+    with pytest.raises(b.H2OError, match="multiple of 64"):
+        b.h2o_decode_step_split(c.desc, q, q, q, out, ev, c.split_workspace(), 100)
+    assert c.t_next == 0  # rejected calls change nothing
+    c.decode_step_split(q, q, q, out, ev)
+    torch.cuda.synchronize()
+    assert c.t_next == 1 and ev.tolist() == [[-1, -1]]
