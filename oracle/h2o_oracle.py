@@ -52,6 +52,15 @@ Policies (the variants the page compares H2O with or reports as worse):
   heavy-hitter-only ablation (H2O §5 "Ablation and Extended Evaluations");
   with k_recent = 0 the new token itself competes and may be the one evicted.
 
+Quantised cache (quant="u8", oracle/quant.py): cached keys and values are
+held as 8-bit codes, keys on per-channel grids fixed by the prompt, values on
+per-token grids (the KIVI finding in Discoveries (cursor 150); H2O combined
+with quantisation, H2O §5). Attention reads the dequantised rows; the new
+token attends to its own key and value at full precision and is quantised
+when it is written into its slot. Scores, selection and eviction are as
+above. An empty prompt leaves nothing to calibrate the key grids on, so a
+quantised cache needs a prompt of at least one token.
+
 Pins: brute force on tiny inputs, the q = 0 closed form, textbook special
 cases (full cache = causal attention, k_heavy = 0 = sliding window, the
 position policy = sink-plus-window attention), the budget-3 illustration of
@@ -62,6 +71,8 @@ from __future__ import annotations
 from dataclasses import dataclass
 
 import numpy as np
+
+from . import quant as qz
 
 __all__ = ["causal_attention_probs", "prefill_column_sums", "select_prefill", "retention_value",
            "eligible_slots", "choose_victim", "H2OOracle", "PrefillResult", "StepResult", "POLICIES"]
@@ -198,12 +209,15 @@ class H2OOracle:
     """
 
     def __init__(self, n_heads: int, head_dim: int, k_heavy: int, k_recent: int, scale: float,
-                 policy: str = "accumulated"):
+                 policy: str = "accumulated", quant: str | None = None):
         if k_heavy < 0 or k_recent < 0 or k_heavy + k_recent < 1:
             raise ValueError("need k_heavy >= 0, k_recent >= 0 and k >= 1")
         if policy not in POLICIES:
             raise ValueError(f"unknown policy {policy!r}")
+        if quant not in (None, "u8"):
+            raise ValueError(f"unknown quantisation {quant!r}")
         self.policy = policy
+        self.quant = quant
         self.G, self.d = n_heads, head_dim
         self.k_heavy, self.k_recent = k_heavy, k_recent
         self.k = k_heavy + k_recent
@@ -214,6 +228,30 @@ class H2OOracle:
         self.pos = np.full((self.G, self.k), -1, dtype=np.int64)
         self.n_used = 0
         self.t = 0
+        if quant:
+            # codes of the cached rows and their grids (K and V above hold the dequantised rows)
+            self.Kq = np.zeros((self.G, self.k, self.d), np.uint8)
+            self.Vq = np.zeros((self.G, self.k, self.d), np.uint8)
+            self.k_scale = np.zeros((self.G, self.d), np.float32)
+            self.k_min = np.zeros((self.G, self.d), np.float32)
+            self.v_scale = np.zeros((self.G, self.k), np.float32)
+            self.v_min = np.zeros((self.G, self.k), np.float32)
+
+    def _store_rows(self, g, slots, k_rows, v_rows):
+        """Write rows into slots of head g (quantised when the cache is)."""
+        if not self.quant:
+            self.K[g, slots] = k_rows
+            self.V[g, slots] = v_rows
+            return
+        k_rows32 = np.asarray(k_rows, np.float32)  # float32-exact inputs
+        v_rows32 = np.asarray(v_rows, np.float32)
+        kc = qz.quantize(k_rows32, self.k_scale[g], self.k_min[g])
+        vs, vm = qz.row_grid(v_rows32)
+        vc = qz.quantize(v_rows32, vs[..., None], vm[..., None])
+        self.Kq[g, slots], self.Vq[g, slots] = kc, vc
+        self.v_scale[g, slots], self.v_min[g, slots] = vs, vm
+        self.K[g, slots] = qz.dequantize(kc, self.k_scale[g], self.k_min[g])
+        self.V[g, slots] = qz.dequantize(vc, vs[..., None], vm[..., None])
 
     def prefill(self, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> PrefillResult:
         """Score the prompt and seed the cache (H2O §A "Pseudocode"); Q, K, V are [G, n, d]."""
@@ -221,6 +259,8 @@ class H2OOracle:
         K = np.asarray(K, np.float64)
         V = np.asarray(V, np.float64)
         n = Q.shape[1]
+        if self.quant and n == 0:
+            raise ValueError("a quantised cache needs a prompt of at least one token")
         colsum = np.zeros((self.G, n))
         margin = np.full(self.G, np.inf)
         self.score[:] = 0.0
@@ -233,8 +273,9 @@ class H2OOracle:
             m = keep.size
             self.pos[g, :m] = keep
             self.score[g, :m] = colsum[g][keep]
-            self.K[g, :m] = K[g][keep]
-            self.V[g, :m] = V[g][keep]
+            if self.quant:
+                self.k_scale[g], self.k_min[g] = qz.channel_grid(K[g])
+            self._store_rows(g, np.arange(m), K[g][keep], V[g][keep])
         self.n_used = min(n, self.k)
         self.t = n
         return PrefillResult(colsum, margin)
@@ -282,8 +323,8 @@ class H2OOracle:
 
         ins = slot >= 0
         r, sl = rows[ins], slot[ins]
-        self.K[r, sl] = k_new[ins]
-        self.V[r, sl] = v_new[ins]
+        for g, s_ in zip(r, sl):
+            self._store_rows(g, np.array([s_]), k_new[g][None], v_new[g][None])
         self.pos[r, sl] = self.t
         self.score[r, sl] = p[ins, nu]
         self.t += 1
@@ -291,5 +332,9 @@ class H2OOracle:
 
     def snapshot(self) -> dict:
         """Copy of the full state (used to resync another implementation)."""
-        return dict(K=self.K.copy(), V=self.V.copy(), score=self.score.copy(),
+        snap = dict(K=self.K.copy(), V=self.V.copy(), score=self.score.copy(),
                     pos=self.pos.copy(), n_used=self.n_used, t=self.t)
+        if self.quant:
+            snap.update(Kq=self.Kq.copy(), Vq=self.Vq.copy(), k_scale=self.k_scale.copy(),
+                        k_min=self.k_min.copy(), v_scale=self.v_scale.copy(), v_min=self.v_min.copy())
+        return snap

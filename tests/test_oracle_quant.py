@@ -1,0 +1,121 @@
+"""Pins of the oracle's 8-bit quantised cache (CPU only).
+
+The quantiser is pinned by values worked out by hand (grids with exact
+scales, round-half-even ties, clamping, a constant row) and by its error
+bound; the quantised H2O oracle is pinned against the plain one, which the
+brute-force and closed-form pins already hold: on inputs that lie exactly on
+their grids (per channel for keys, per row for values) quantisation is
+lossless and the two must agree bit for bit, and a new token attends at full
+precision in its own step.
+"""
+import numpy as np
+import pytest
+
+from oracle import H2OOracle
+from oracle import quant as qz
+
+
+def test_codes_on_an_exact_grid():
+    scale, mn = qz.row_grid(np.array([0.0, 255.0], np.float32))
+    assert scale == 1.0 and mn == 0.0
+    x = np.array([0, 1.5, 2.5, 126.5, 127.5, 254.5, 255, -3, 300], np.float32)
+    # round half to even; values outside the grid clamp to its ends
+    assert qz.quantize(x, scale, mn).tolist() == [0, 2, 2, 126, 128, 254, 255, 0, 255]
+    scale, mn = qz.row_grid(np.array([-10.0, 500.0], np.float32))  # 510 / 255 = 2
+    assert scale == 2.0 and mn == -10.0
+    assert qz.quantize(np.array([-7, -5, 0, 499], np.float32), scale, mn).tolist() == [2, 2, 5, 254]
+    assert qz.dequantize(np.array([0, 5, 255], np.uint8), scale, mn).tolist() == [-10.0, 0.0, 500.0]
+
+
+def test_constant_row_and_channel():
+    scale, mn = qz.row_grid(np.full(8, 7.0, np.float32))
+    assert scale == 0.0 and mn == 7.0
+    codes = qz.quantize(np.full(8, 7.0, np.float32), scale, mn)
+    assert codes.tolist() == [0] * 8
+    assert np.all(qz.dequantize(codes, scale, mn) == 7.0)
+    ks, km = qz.channel_grid(np.array([[1.0, 2.0], [1.0, 6.0]], np.float32))
+    assert ks.tolist() == [0.0, np.float32(4.0) / np.float32(255)] and km.tolist() == [1.0, 2.0]
+
+
+def test_error_bound_and_ends():
+    rng = np.random.default_rng(5)
+    V = (rng.standard_normal((200, 128)) * rng.uniform(0.1, 10, (200, 1))).astype(np.float32)
+    s, m = qz.row_grid(V)
+    c = qz.quantize(V, s[:, None], m[:, None])
+    err = np.abs(qz.dequantize(c, s[:, None], m[:, None]) - V)
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+    assert np.all(c[np.arange(200), V.argmin(1)] == 0)
+    assert np.all(c[np.arange(200), V.argmax(1)] == 255)
+    K = rng.standard_normal((300, 64)).astype(np.float32)
+    ks, km = qz.channel_grid(K)
+    kc = qz.quantize(K, ks, km)
+    assert np.all(np.abs(qz.dequantize(kc, ks, km) - K) <= ks * (0.5 + 1e-5))
+    assert np.all(kc.min(0) == 0) and np.all(kc.max(0) == 255)
+
+
+def _grid_inputs(rng, G, n, T, d):
+    """Keys on per-channel grids with power-of-two steps fixed by the prompt
+    (every channel's prompt column holds codes 0 and 255); values on per-row
+    grids (every row holds codes 0 and 255)."""
+    step = 2.0 ** rng.integers(-6, -2, (G, 1, d))
+    base = step * rng.integers(-200, -100, (G, 1, d))
+    kc = rng.integers(0, 256, (G, n + T, d))
+    kc[:, 0], kc[:, 1] = 0, 255
+    K = base + step * kc
+    vstep = 2.0 ** rng.integers(-6, -2, (G, n + T, 1))
+    vc = rng.integers(0, 256, (G, n + T, d))
+    vc[..., 0], vc[..., 1] = 0, 255
+    V = vstep * (vc - rng.integers(100, 200, (G, n + T, 1)))
+    Q = rng.standard_normal((G, n + T, d))
+    return Q, K, V
+
+
+@pytest.mark.parametrize("policy,kh,kr", [("accumulated", 5, 4), ("averaged", 3, 3), ("accumulated", 6, 0)])
+def test_quantised_equals_plain_on_grid_inputs(policy, kh, kr):
+    rng = np.random.default_rng(11)
+    G, n, T, d = 3, 20, 25, 16
+    Q, K, V = _grid_inputs(rng, G, n, T, d)
+    scale = 0.3
+    plain = H2OOracle(G, d, kh, kr, scale, policy)
+    quant = H2OOracle(G, d, kh, kr, scale, policy, quant="u8")
+    a, b = plain.prefill(Q[:, :n], K[:, :n], V[:, :n]), quant.prefill(Q[:, :n], K[:, :n], V[:, :n])
+    assert np.array_equal(a.colsum, b.colsum)
+    assert np.array_equal(plain.K, quant.K) and np.array_equal(plain.V, quant.V)
+    for t in range(T):
+        i = n + t
+        sa = plain.decode_step(Q[:, i], K[:, i], V[:, i])
+        sb = quant.decode_step(Q[:, i], K[:, i], V[:, i])
+        assert np.array_equal(sa.evicted, sb.evicted)
+        assert np.array_equal(sa.out, sb.out)
+        assert np.array_equal(plain.score, quant.score) and np.array_equal(plain.pos, quant.pos)
+    assert np.array_equal(plain.K, quant.K) and np.array_equal(plain.V, quant.V)
+
+
+def test_new_token_attends_at_full_precision_then_is_quantised():
+    rng = np.random.default_rng(12)
+    G, n, d = 2, 12, 16
+    Q, K, V = _grid_inputs(rng, G, n, 1, d)
+    plain = H2OOracle(G, d, 4, 4, 0.25)
+    quant = H2OOracle(G, d, 4, 4, 0.25, quant="u8")
+    plain.prefill(Q[:, :n], K[:, :n], V[:, :n])
+    quant.prefill(Q[:, :n], K[:, :n], V[:, :n])
+    # an off-grid new token, its key partly outside the prompt's channel range
+    k_new = rng.standard_normal((G, d)) * 3
+    k_new[:, 0] = 1e3
+    v_new = rng.standard_normal((G, d))
+    q = rng.standard_normal((G, d))
+    sa, sb = plain.decode_step(q, k_new, v_new), quant.decode_step(q, k_new, v_new)
+    assert np.array_equal(sa.out, sb.out) and np.array_equal(sa.evicted, sb.evicted)
+    for g in range(G):
+        s = sb.slot[g]
+        kmax = (quant.k_min[g].astype(np.float64) + 255 * quant.k_scale[g].astype(np.float64))
+        assert quant.Kq[g, s, 0] == 255 and quant.K[g, s, 0] == kmax[0]  # clamped to the grid's top
+        assert np.all(np.abs(quant.K[g, s] - np.clip(k_new[g], quant.k_min[g], kmax))
+                      <= quant.k_scale[g] * (0.5 + 1e-5))
+        assert np.all(np.abs(quant.V[g, s] - v_new[g]) <= quant.v_scale[g, s] * (0.5 + 1e-5) + 1e-6)
+
+
+def test_quantised_cache_needs_a_prompt():
+    o = H2OOracle(1, 16, 2, 2, 0.25, quant="u8")
+    with pytest.raises(ValueError):
+        o.prefill(np.zeros((1, 0, 16)), np.zeros((1, 0, 16)), np.zeros((1, 0, 16)))
