@@ -32,7 +32,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
 METRIC = "H2O decode head-steps/sec + achieved HBM GB/s (% of MI355X peak)"
 DECODE_SOURCES = {"fused": ["decode.hip", "h2o_device.h", "launch.h"],
-                  "split": ["decode_split.hip", "h2o_device.h", "launch.h"]}
+                  "split": ["decode_split.hip", "h2o_device.h", "launch.h"],
+                  "u8": ["decode_u8.hip", "h2o_device.h", "launch.h"]}
 
 
 def log(*a):
@@ -53,6 +54,8 @@ def parse_args():
     p.add_argument("--decode", choices=("fused", "split"), default="fused",
                    help="decode entry point: h2o_decode_step (fused) or h2o_decode_step_split")
     p.add_argument("--chunk-rows", type=int, default=0, help="split decode chunk length (0 = library's choice)")
+    p.add_argument("--quant", choices=("none", "u8"), default="none",
+                   help="cache storage: rows in the workload dtype, or 8-bit codes (h2o_cache_init_u8)")
     p.add_argument("--cpu-heads", type=int, default=256, help="heads in the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-single-layer", action="store_true")
@@ -79,8 +82,15 @@ def decode_bytes_per_head(n_used: int, d: int, e: int) -> int:
     return 2 * n_used * d * e + 12 * n_used + 5 * d * e + 4 * d + 8
 
 
+def decode_bytes_per_head_u8(n_used: int, d: int, e: int) -> int:
+    """The same for an 8-bit cache: codes instead of rows, plus the value grid
+    of every occupied slot and the head's key grids; the new token's codes and
+    value grid are written."""
+    return 2 * n_used * d + 8 * n_used + 12 * n_used + 3 * d * e + 8 * d + 4 * d + 2 * d + 8 + 8
+
+
 def load_traffic(workload: str, digest: str, mode: str = "fused"):
-    name = f"decode_{workload}" if mode == "fused" else f"decode_split_{workload}"
+    name = f"decode_{workload}" if mode == "fused" else f"decode_{mode}_{workload}"
     path = os.path.join(ROOT, "profiles", f"{name}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -172,7 +182,11 @@ def main():
 
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
-    caches = [H2OCache(B, H, d, wl.k_heavy, wl.k_recent, tdt, wl.scale, dev) for _ in range(L)]
+    quant = args.quant == "u8"
+    if quant and args.decode == "split":
+        raise SystemExit("the split decode entry point takes caches stored in their dtype only")
+    caches = [H2OCache(B, H, d, wl.k_heavy, wl.k_recent, tdt, wl.scale, dev, quant="u8" if quant else None)
+              for _ in range(L)]
     ws = caches[0].workspace(n)
     outs = [torch.empty(B, H, d, dtype=torch.float32, device=dev) for _ in range(L)]
     evs = [torch.empty(B, H, dtype=torch.int32, device=dev) for _ in range(L)]
@@ -191,9 +205,15 @@ def main():
         """Whole path for `layers` caches: clear, prefill, T decode steps."""
         for i in layers:
             c = caches[i]
-            check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
-                                     ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
-                                     c.score.data_ptr(), c.pos.data_ptr(), sh))
+            if quant:
+                check(lib.h2o_cache_init_u8(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
+                                            ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
+                                            c.k_qparam.data_ptr(), c.v_qparam.data_ptr(),
+                                            c.score.data_ptr(), c.pos.data_ptr(), sh))
+            else:
+                check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
+                                         ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
+                                         c.score.data_ptr(), c.pos.data_ptr(), sh))
             check(lib.h2o_prefill_select(ctypes.byref(c.desc), Q.data_ptr(), K.data_ptr(), V.data_ptr(), n,
                                          ws.data_ptr(), ws.numel(), None, sh))
         if ev is not None:
@@ -232,12 +252,14 @@ def main():
     value = head_steps / (ms_per_step / 1e3)
 
     n_used = [min(k, n + t) for t in range(T)]
-    bytes_per_launch = G * sum(decode_bytes_per_head(u, d, e) for u in n_used) / T
+    per_head = decode_bytes_per_head_u8 if quant else decode_bytes_per_head
+    bytes_per_launch = G * sum(per_head(u, d, e) for u in n_used) / T
     launches = T * L
     avg_launch_s = (sum(decode_ms) / args.steps) / 1e3 / launches
     achieved = bytes_per_launch / avg_launch_s / 1e9
-    digest = decode_source_digest(args.decode)
-    traffic = load_traffic(wl.name, digest, args.decode) if args.batch is None and args.heads is None else None
+    mode = "u8" if quant else args.decode
+    digest = decode_source_digest(mode)
+    traffic = load_traffic(wl.name, digest, mode) if args.batch is None and args.heads is None else None
     prefill_flops = 2.0 * n * (n + 1) * d * G  # two causal QK^T passes per layer
     pf_s = (sum(prefill_ms) / args.steps) / 1e3 / L
 
@@ -272,11 +294,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "heads": H, "head_dim": d, "prompt_len": n,
                    "k_heavy": wl.k_heavy, "k_recent": wl.k_recent, "decode_steps": T, "layers": L,
-                   "pareto_alpha": wl.alpha, "parallelism": "none (1 GPU)", "decode_entry": args.decode},
+                   "pareto_alpha": wl.alpha, "parallelism": "none (1 GPU)", "decode_entry": args.decode,
+                   "cache_storage": "u8 codes" if quant else wl.dtype},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": ("h2o decode_split_kernel (chunked attention, last chunk merges + scores + "
-                                "evicts + inserts)" if split else
+                     "kernel": ("h2o decode_chunk_kernel + decode_merge_kernel (split decode)" if split else
+                                "h2o decode_u8_kernel (fused step over 8-bit codes)" if quant else
                                 "h2o decode_kernel (fused attention + score + evict + insert)"),
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
                      "kernel_source_digest": digest},

@@ -64,6 +64,23 @@ typedef enum { H2O_F32 = 0, H2O_BF16 = 1, H2O_F16 = 2 } h2o_dtype;
  */
 typedef enum { H2O_POLICY_ACCUMULATED = 0, H2O_POLICY_AVERAGED = 1, H2O_POLICY_POSITION = 2 } h2o_policy;
 
+/*
+ * Storage of a cache's keys and values:
+ *   NONE - rows in the cache dtype, as handed in;
+ *   U8   - 8-bit codes (H2O combined with quantisation, H2O §5 "Ablation and
+ *          Extended Evaluations"; keys per channel and values per token, after
+ *          the KIVI abstract on the page "Discoveries (cursor 150)"). Keys use
+ *          one affine grid per (batch, head, channel), fixed by the prompt:
+ *          mn_c and mx_c are the prompt's smallest and largest key values in
+ *          channel c and scale_c = (mx_c - mn_c) / 255. Values use one grid per
+ *          cached row over its own d values. A value x is stored as the code
+ *          rint((x - mn) / scale) clamped to [0, 255] (0 if scale = 0), all in
+ *          fp32 with IEEE rounding and ties to even, and read as
+ *          code * scale + mn. A decode token attends to its own key and value
+ *          at full precision; it is quantised when written into its slot.
+ */
+typedef enum { H2O_QUANT_NONE = 0, H2O_QUANT_U8 = 1 } h2o_quant;
+
 /* Limits of this build. */
 #define H2O_MAX_SLOTS 8192      /* k = k_heavy + k_recent */
 #define H2O_MAX_PROMPT 1048576  /* n */
@@ -97,7 +114,9 @@ typedef struct {
   int32_t t_next;
   int64_t steps;    /* decode steps taken since init */
   uint32_t magic;   /* set by h2o_cache_init */
-  uint32_t reserved;
+  int32_t quant;    /* h2o_quant */
+  float* k_qparam;  /* U8 only: [batch][heads][2][head_dim] fp32, key grid scale_c then mn_c */
+  float* v_qparam;  /* U8 only: [batch][heads][k][2] fp32, value grid (scale, mn) of each slot */
 } h2o_cache;
 
 typedef struct {
@@ -119,6 +138,22 @@ h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_
                           int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype,
                           float scale, void* K, void* V, float* score, int32_t* pos,
                           h2o_stream_t stream);
+
+/*
+ * As h2o_cache_init, for a cache stored as 8-bit codes (H2O_QUANT_U8, see
+ * h2o_quant). dtype is that of the queries, keys and values handed to prefill
+ * and decode; the cache holds
+ *   Kq, Vq   : [batch][heads][k][head_dim] uint8 codes, slot-indexed rows
+ *   k_qparam : [batch][heads][2][head_dim] fp32, written by prefill
+ *   v_qparam : [batch][heads][k][2] fp32
+ * with score and pos as for h2o_cache_init. Kq, Vq, k_qparam and v_qparam
+ * must be 16-byte aligned. The prompt handed to prefill must have n >= 1
+ * (it fixes the key grids). h2o_decode_step_split does not take such a cache.
+ */
+h2o_status h2o_cache_init_u8(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                             int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype,
+                             float scale, uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam,
+                             float* score, int32_t* pos, h2o_stream_t stream);
 
 /* Bytes of device workspace h2o_prefill_select needs for a prompt of n tokens. */
 size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n);

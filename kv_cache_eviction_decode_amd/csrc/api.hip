@@ -46,15 +46,9 @@ constexpr int kSplitRows = 64;
 size_t split_cmax(int32_t k) { return (size_t(k) + kSplitRows - 1) / kSplitRows; }
 static_assert((H2O_MAX_SLOTS + kSplitRows - 1) / kSplitRows <= h2o::kMaxChunks, "split chunk capacity");
 
-}  // namespace
-
-extern "C" {
-
-const char* h2o_last_error(void) { return g_err; }
-
-h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
-                          int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
-                          void* K, void* V, float* score, int32_t* pos, h2o_stream_t stream) {
+h2o_status init_cache(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim, int32_t k_heavy,
+                      int32_t k_recent, int32_t policy, int32_t dtype, float scale, void* K, void* V, float* score,
+                      int32_t* pos, int32_t quant, float* k_qparam, float* v_qparam, h2o_stream_t stream) {
   if (!cache) return fail(H2O_EINVAL, "cache is NULL");
   if (batch < 1 || heads < 1) return fail(H2O_EINVAL, "batch and heads must be >= 1");
   if (int64_t(batch) * heads > (int64_t(1) << 31) - 1) return fail(H2O_EINVAL, "batch*heads too large");
@@ -89,12 +83,39 @@ h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_
   c.t_next = 0;
   c.steps = 0;
   c.magic = kMagic;
+  c.quant = quant;
+  c.k_qparam = k_qparam;
+  c.v_qparam = v_qparam;
   const int64_t count = int64_t(batch) * heads * (k_heavy + k_recent);
   h2o_status st = device_status(
       h2o::launch_cache_clear(score, pos, count, static_cast<hipStream_t>(stream)), "h2o_cache_init");
   if (st != H2O_OK) return st;
   *cache = c;
   return H2O_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* h2o_last_error(void) { return g_err; }
+
+h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                          int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
+                          void* K, void* V, float* score, int32_t* pos, h2o_stream_t stream) {
+  return init_cache(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, K, V, score, pos,
+                    H2O_QUANT_NONE, nullptr, nullptr, stream);
+}
+
+h2o_status h2o_cache_init_u8(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                             int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
+                             uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam, float* score,
+                             int32_t* pos, h2o_stream_t stream) {
+  if (!k_qparam || !v_qparam) return fail(H2O_EINVAL, "k_qparam and v_qparam must be non-NULL");
+  if (!aligned(k_qparam, 16) || !aligned(v_qparam, 16))
+    return fail(H2O_EINVAL, "k_qparam and v_qparam must be 16-byte aligned");
+  return init_cache(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, Kq, Vq, score, pos,
+                    H2O_QUANT_U8, k_qparam, v_qparam, stream);
 }
 
 size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n) {
@@ -110,6 +131,8 @@ h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, c
   if (st != H2O_OK) return st;
   if (cache->t_next != 0) return fail(H2O_ESTATE, "prefill needs a freshly initialised cache (t_next = %d)", cache->t_next);
   if (n < 0 || n > H2O_MAX_PROMPT) return fail(H2O_EINVAL, "prompt length %d out of range [0, %d]", n, H2O_MAX_PROMPT);
+  if (n == 0 && cache->quant != H2O_QUANT_NONE)
+    return fail(H2O_EINVAL, "an 8-bit cache needs a prompt of at least one token (it fixes the key grids)");
   if (n == 0) return H2O_OK;  // nothing to score; the cleared cache is the result
   if (!Q || !Kp || !Vp) return fail(H2O_EINVAL, "Q, K and V must be non-NULL");
   if (!aligned(Q, 16) || !aligned(Kp, 16) || !aligned(Vp, 16))
@@ -138,6 +161,9 @@ h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, c
   a.k_recent = cache->k_recent;
   a.policy = cache->policy;
   a.c = cache->scale * h2o::kLog2e;
+  a.quant = cache->quant;
+  a.kq_param = cache->k_qparam;
+  a.vq_param = cache->v_qparam;
   st = device_status(h2o::launch_prefill(cache->dtype, cache->head_dim, G, a, static_cast<hipStream_t>(stream)),
                      "h2o_prefill_select");
   if (st != H2O_OK) return st;
@@ -176,8 +202,12 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, c
   a.k_recent = cache->k_recent;
   a.policy = cache->policy;
   a.c = cache->scale * h2o::kLog2e;
-  st = device_status(h2o::launch_decode(cache->dtype, cache->head_dim, cache->batch * cache->heads, a,
-                                        static_cast<hipStream_t>(stream)),
+  a.k_qparam = cache->k_qparam;
+  a.v_qparam = cache->v_qparam;
+  const int G = cache->batch * cache->heads;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = device_status(cache->quant == H2O_QUANT_U8 ? h2o::launch_decode_u8(cache->dtype, cache->head_dim, G, a, s)
+                                                  : h2o::launch_decode(cache->dtype, cache->head_dim, G, a, s),
                      "h2o_decode_step");
   if (st != H2O_OK) return st;
   cache->t_next += 1;
@@ -203,6 +233,7 @@ h2o_status h2o_decode_step_split(h2o_cache* cache, const void* q, const void* k_
     return fail(H2O_EINVAL, "q, k_new, v_new, out and evicted_pos must be non-NULL");
   if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) || !aligned(evicted_pos, 4))
     return fail(H2O_EINVAL, "q, k_new, v_new, out must be 16-byte aligned; evicted_pos 4-byte aligned");
+  if (cache->quant != H2O_QUANT_NONE) return fail(H2O_EINVAL, "split decode takes caches stored in their dtype only");
   if (chunk_rows < 0 || chunk_rows % kSplitRows != 0)
     return fail(H2O_EINVAL, "chunk_rows must be 0 or a positive multiple of %d", kSplitRows);
   const int32_t k = cache->k_heavy + cache->k_recent;

@@ -1,0 +1,316 @@
+// H2O decode step over a cache stored as 8-bit codes, for gfx950.
+//
+// Citations ("H2O §x") refer to the page "H2O: Heavy-Hitter Oracle for
+// Efficient Generative Inference of Large Language Models" (paperlayer.ai
+// summary of arXiv 2306.14048v3); the code format (keys on per-channel grids,
+// values on per-token grids) follows the KIVI abstract on the page
+// "Discoveries (cursor 150)" and is described with h2o_quant in the C header.
+//
+// The step is the fused one of decode.hip (attention of the new token over
+// the occupied slots and itself, H2O §D "Recursive attention"; accumulated
+// scores, §1 and §B.2; at most one eviction outside the recent window, §2
+// "Problem formulation", §D "Cache eviction"; insert into the freed slot),
+// reading codes instead of rows. The grids fold into the arithmetic instead
+// of being applied per element:
+//   q.k_a   = sum_c q_c (s_c code_ac + mn_c) = sum_c (q_c s_c) code_ac + sum_c q_c mn_c,
+//             so each head pre-scales q by the key grid once and adds one bias;
+//   p_a v_a = (p_a s_a) code_a + (p_a mn_a) 1, so the P.V accumulator takes
+//             p_a s_a per row and a separate sum of p_a mn_a.
+// A row of d codes is read by d/16 lanes (16 codes each), one wave per head,
+// persistent over heads, two batches of rows in flight as in the wave kernel
+// of decode.hip. The new token's key and value are quantised on insert.
+
+#include "h2o_device.h"
+#include "launch.h"
+
+namespace h2o {
+namespace {
+
+__device__ __forceinline__ void codes_to_float(uint4 w, float (&c)[16]) {
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[4 * i] = float(v[i] & 0xFFu);
+    c[4 * i + 1] = float((v[i] >> 8) & 0xFFu);
+    c[4 * i + 2] = float((v[i] >> 16) & 0xFFu);
+    c[4 * i + 3] = float(v[i] >> 24);
+  }
+}
+
+__device__ __forceinline__ uint4 pack_codes(const uint32_t (&c)[16]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = c[4 * i] | c[4 * i + 1] << 8 | c[4 * i + 2] << 16 | c[4 * i + 3] << 24;
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// 16 consecutive elements of a dtype row as fp32.
+template <int DT> __device__ __forceinline__ void load16(const void* row, int first, float (&x)[16]) {
+  constexpr int E = Elem<DT>::bytes, EPC = 16 / E;  // elements per 16-byte chunk
+  const char* p = static_cast<const char*>(row) + size_t(first) * E;
+#pragma unroll
+  for (int i = 0; i < 16 / EPC; ++i) Unpack<DT>::run(ld16(p + 16 * i), x + EPC * i);
+}
+
+// One wave per head.
+//   UB: wave-loads of codes (1 KiB of K and 1 KiB of V) per batch; PF: score/pos
+//   entries per lane prefetched with the head's inputs.
+template <int DT, int D, int UB, int PF>
+__global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
+  constexpr int LPR = D / 16;    // lanes per row of codes
+  constexpr int RPU = 64 / LPR;  // rows per wave-wide load
+  extern __shared__ float sm_logit[];  // [k] logits of the current head, base-2 units
+  const int lane = threadIdx.x;
+  const int grp = lane / LPR;
+  const int sub = lane % LPR;
+  const int c0 = sub * 16;  // this lane's channels
+  const int nu = a.n_used;
+  const int units = (nu + RPU - 1) / RPU;
+  const int nb = (units + UB - 1) / UB;
+
+  for (int head = blockIdx.x; head < G; head += gridDim.x) {
+    const size_t hrow = size_t(head) * a.k;
+    // ---- head inputs: q folded with the key grid, the new token, scores ---------------
+    const float* kg = a.k_qparam + size_t(head) * 2 * D + c0;  // this lane's key grids
+    float qs[16];
+    float bias;
+    {
+      float q[16];
+      load16<DT>(static_cast<const char*>(a.q) + size_t(head) * D * Elem<DT>::bytes, c0, q);
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        qs[i] = q[i] * kg[i] * a.c;
+        part = fmaf(q[i], kg[D + i], part);
+      }
+      bias = group_sum<LPR>(part) * a.c;
+    }
+    float sc_pf[PF];
+    int pos_pf[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int slot = lane + 64 * i;
+      sc_pf[i] = 0.f;
+      pos_pf[i] = 0;
+      if (slot < nu) {
+        sc_pf[i] = a.score[hrow + slot];
+        pos_pf[i] = a.pos[hrow + slot];
+      }
+    }
+
+    // ---- stream the codes: per lane-group online softmax -------------------------------
+    const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * D + c0;
+    const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * D + c0;
+    const float2* vg = reinterpret_cast<const float2*>(a.v_qparam) + hrow;
+    float m = kNegInf, l = 0.f, pm = 0.f;  // pm: sum of p * value-grid minimum
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    // Loads are unconditional (clamped to the last occupied row, masked) so
+    // that the compiler's wait counts stay exact.
+    auto issue = [&](uint4 (&kb)[UB], uint4 (&vb)[UB], float2 (&gb)[UB], int b) {
+#pragma unroll
+      for (int j = 0; j < UB; ++j) {
+        const int row = min((b * UB + j) * RPU + grp, nu - 1);
+        kb[j] = ld16(Kh + size_t(row) * D);
+        vb[j] = ld16(Vh + size_t(row) * D);
+        gb[j] = vg[row];
+      }
+    };
+    auto compute = [&](const uint4 (&kb)[UB], const uint4 (&vb)[UB], const float2 (&gb)[UB], int b) {
+      float s[UB];
+      float bm = kNegInf;
+#pragma unroll
+      for (int j = 0; j < UB; ++j) {
+        const int row = (b * UB + j) * RPU + grp;
+        float c[16];
+        codes_to_float(kb[j], c);
+        float x = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x = fmaf(qs[i], c[i], x);
+        x = group_sum<LPR>(x) + bias;
+        s[j] = row < nu ? x : kNegInf;
+        bm = fmaxf(bm, s[j]);
+        if (sub == 0 && row < nu) sm_logit[row] = s[j];
+      }
+      if (bm != kNegInf) {
+        const float mn = fmaxf(m, bm);
+        const float alpha = fast_exp2(m - mn);
+        l *= alpha;
+        pm *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] *= alpha;
+#pragma unroll
+        for (int j = 0; j < UB; ++j) {
+          const float p = fast_exp2(s[j] - mn);
+          l += p;
+          pm = fmaf(p, gb[j].y, pm);
+          const float ps = p * gb[j].x;
+          float c[16];
+          codes_to_float(vb[j], c);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[i] = fmaf(ps, c[i], acc[i]);
+        }
+        m = mn;
+      }
+    };
+    if (nb > 0) {
+      uint4 kA[UB], vA[UB], kB[UB], vB[UB];
+      float2 gA[UB], gB[UB];
+      issue(kA, vA, gA, 0);
+      for (int b = 0; b < nb; b += 2) {
+        set_wave_priority(3 - (4 * b) / nb);  // lagging waves of a SIMD issue first
+        issue(kB, vB, gB, b + 1);
+        compute(kA, vA, gA, b);
+        issue(kA, vA, gA, b + 2);
+        compute(kB, vB, gB, b + 1);
+      }
+    }
+
+    // ---- merge the lane groups, output -------------------------------------------------
+    float qf[16], kn[16], vn[16];
+    load16<DT>(static_cast<const char*>(a.q) + size_t(head) * D * Elem<DT>::bytes, c0, qf);
+    load16<DT>(static_cast<const char*>(a.k_new) + size_t(head) * D * Elem<DT>::bytes, c0, kn);
+    load16<DT>(static_cast<const char*>(a.v_new) + size_t(head) * D * Elem<DT>::bytes, c0, vn);
+    float sn = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sn = fmaf(qf[i], kn[i], sn);
+    const float s_new = group_sum<LPR>(sn) * a.c;  // the new token at full precision
+    const float M = fmaxf(across_groups<LPR>(m, OpMax()), s_new);
+    const float w = fast_exp2(m - M);
+    const float lw = across_groups<LPR>(l * w, OpAdd());
+    const float pmw = across_groups<LPR>(pm * w, OpAdd());
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = across_groups<LPR>(acc[i] * w, OpAdd());
+    const float w_new = fast_exp2(s_new - M);
+    const float invZ = 1.0f / (lw + w_new);
+    if (grp == 0) {
+      float* op = a.out + size_t(head) * D + c0;
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (acc[i + e] + pmw + w_new * vn[i + e]) * invZ;
+        *reinterpret_cast<float4*>(op + i) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+
+    // ---- accumulate scores, pick the victim ------------------------------------------
+    const float p_new = w_new * invZ;
+    const bool full = nu == a.k;
+    const int lim = a.t - a.k_recent;
+    float* sc_g = a.score + hrow;
+    int32_t* pos_g = a.pos + hrow;
+    uint64_t best = ~0ull;
+    int best_slot = -1, best_pos = -1;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int slot = lane + 64 * i;
+      if (slot < nu) {
+        const float sc = sc_pf[i] + fast_exp2(sm_logit[slot] - M) * invZ;
+        sc_g[slot] = sc;
+        if (full && pos_pf[i] <= lim) {
+          const uint64_t key = evict_key(sc, pos_pf[i], a.t, a.policy);
+          if (key < best) {
+            best = key;
+            best_slot = slot;
+            best_pos = pos_pf[i];
+          }
+        }
+      }
+    }
+    for (int slot = lane + 64 * PF; slot < nu; slot += 64) {
+      const float sc = sc_g[slot] + fast_exp2(sm_logit[slot] - M) * invZ;
+      const int ps = pos_g[slot];
+      sc_g[slot] = sc;
+      if (full && ps <= lim) {
+        const uint64_t key = evict_key(sc, ps, a.t, a.policy);
+        if (key < best) {
+          best = key;
+          best_slot = slot;
+          best_pos = ps;
+        }
+      }
+    }
+    // Without a recent window the new token competes too (slot k = "itself").
+    if (full && a.k_recent == 0 && lane == 0) {
+      const uint64_t key = evict_key(p_new, a.t, a.t, a.policy);
+      if (key < best) {
+        best = key;
+        best_slot = a.k;
+        best_pos = a.t;
+      }
+    }
+    int victim = nu;
+    int evicted = -1;
+    if (full) {
+      const uint64_t gmin = wave_min_u64(best);
+      // Keys are unique (positions are), so exactly one lane holds the minimum.
+      const uint64_t owners = __ballot(best == gmin && gmin != ~0ull);
+      if (owners) {
+        const int owner = __ffsll((unsigned long long)owners) - 1;
+        victim = __builtin_amdgcn_readlane(best_slot, owner);
+        evicted = __builtin_amdgcn_readlane(best_pos, owner);
+      } else {
+        victim = -1;  // no eligible slot: the caller's state is inconsistent
+        evicted = -2;
+      }
+    }
+
+    // ---- insert the new token, quantised ---------------------------------------------
+    if (victim >= 0 && victim < a.k) {
+      if (lane == victim % 64) {
+        sc_g[victim] = p_new;
+        pos_g[victim] = a.t;
+      }
+      float vmn = vn[0], vmx = vn[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        vmn = fminf(vmn, vn[i]);
+        vmx = fmaxf(vmx, vn[i]);
+      }
+      vmn = lane_group<LPR>(vmn, OpMin());
+      vmx = lane_group<LPR>(vmx, OpMax());
+      const float vs = u8_grid_scale(vmn, vmx);
+      if (grp == 0) {
+        uint32_t kc[16], vc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          kc[i] = quantize_u8(kn[i], kg[i], kg[D + i]);
+          vc[i] = quantize_u8(vn[i], vs, vmn);
+        }
+        st16(static_cast<uint8_t*>(a.K_w) + (hrow + victim) * D + c0, pack_codes(kc));
+        st16(static_cast<uint8_t*>(a.V_w) + (hrow + victim) * D + c0, pack_codes(vc));
+        if (sub == 0) reinterpret_cast<float2*>(a.v_qparam)[hrow + victim] = make_float2(vs, vmn);
+      }
+    }
+    if (lane == 0) a.evicted[head] = evicted;
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
+  constexpr int UB = 4, PF = 4, MINW = 2;
+  const int resident = cu_count() * 4 * MINW;
+  const int grid = G < resident ? G : resident;
+  const size_t shmem = size_t(a.k) * sizeof(float);
+  hipLaunchKernelGGL((decode_u8_kernel<DT, D, UB, PF>), dim3(grid), dim3(64), shmem, s, a, G);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_u8(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s) {
+  if (G <= 0) return hipSuccess;
+  switch (dtype * 1000 + head_dim) {
+    case DT_F32 * 1000 + 64: return launch_typed<DT_F32, 64>(G, a, s);
+    case DT_F32 * 1000 + 128: return launch_typed<DT_F32, 128>(G, a, s);
+    case DT_BF16 * 1000 + 64: return launch_typed<DT_BF16, 64>(G, a, s);
+    case DT_BF16 * 1000 + 128: return launch_typed<DT_BF16, 128>(G, a, s);
+    case DT_F16 * 1000 + 64: return launch_typed<DT_F16, 64>(G, a, s);
+    case DT_F16 * 1000 + 128: return launch_typed<DT_F16, 128>(G, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace h2o

@@ -156,10 +156,11 @@ __device__ __forceinline__ LanePair swap32(uint32_t x) {
 constexpr int kRowRor8 = 0x128;  // lane i <- lane (i + 8) mod 16 within each row
 
 // Combine values across the lane groups of N consecutive lanes (N in
-// {8, 16, 32}): lanes at the same position in every group end with the same
+// {4, 8, 16, 32}): lanes at the same position in every group end with the same
 // result. OP is a commutative binary functor on floats.
 template <int N, class OP> __device__ __forceinline__ float across_groups(float x, OP op) {
-  static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  if constexpr (N <= 4) x = op(x, __shfl_xor(x, 4));
   if constexpr (N <= 8) x = op(x, dpp<kRowRor8>(x));
   if constexpr (N <= 16) {
     const LanePair r = swap16(__float_as_uint(x));
@@ -177,6 +178,27 @@ struct OpAdd {
 struct OpMax {
   __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
 };
+struct OpMin {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fminf(a, b); }
+};
+
+// Combine within aligned groups of N consecutive lanes (N a power of two <= 64).
+template <int N, class OP> __device__ __forceinline__ float lane_group(float x, OP op) {
+#pragma unroll
+  for (int off = 1; off < N; off <<= 1) x = op(x, __shfl_xor(x, off));
+  return x;
+}
+
+// ---- 8-bit cache codes (format: h2o_quant in the C header) ----------------------
+// Grid step over [lo, hi] and the code of x: rint((x - mn) / scale) clamped to
+// [0, 255], ties to even, 0 on a degenerate grid. Plain fp32 operations with
+// IEEE rounding (the division is correctly rounded), so the codes are exact.
+__device__ __forceinline__ float u8_grid_scale(float lo, float hi) { return (hi - lo) / 255.0f; }
+__device__ __forceinline__ uint32_t quantize_u8(float x, float scale, float mn) {
+  if (!(scale > 0.f)) return 0;
+  const float q = __builtin_rintf((x - mn) / scale);
+  return uint32_t(fminf(fmaxf(q, 0.f), 255.f));
+}
 
 template <int CTRL> __device__ __forceinline__ uint64_t dpp64(uint64_t x) {
   const uint32_t lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(x)), CTRL, 0xF, 0xF, false);

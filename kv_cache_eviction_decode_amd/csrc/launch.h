@@ -23,6 +23,8 @@ struct DecodeArgs {
   const void* v_new;   // [G][d]           (scored mode only)
   float* out;          // [G][d] fp32
   int32_t* evicted;    // [G]              (scored mode only)
+  const float* k_qparam;  // [G][2][d] key grids (8-bit caches only)
+  float* v_qparam;        // [G][k][2] value grids (8-bit caches only)
   int32_t k;           // slot capacity (rows per head in K/V)
   int32_t n_used;      // occupied slots [0, n_used), or full-cache length
   int32_t t;           // position of the new token
@@ -37,6 +39,9 @@ int cu_count();
 // Fused H2O decode step: attention over n_used slots + the new token, score
 // accumulation, at most one eviction, insert. One workgroup per head.
 hipError_t launch_decode(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);
+
+// Decode step of a cache stored as 8-bit codes (K, V point to the codes).
+hipError_t launch_decode_u8(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);
 
 // Split decode: the occupied slots of every head are cut into `chunks` runs of
 // `chunk_len` rows (the last one ragged), each streamed by its own wave; a
@@ -72,6 +77,9 @@ struct PrefillArgs {
   int32_t k_heavy, k_recent;
   int32_t policy;  // h2o_policy
   float c;         // scale * log2(e)
+  int32_t quant;   // h2o_quant of the cache
+  float* kq_param; // [G][2][d] key grids (8-bit caches)
+  float* vq_param; // [G][k][2] value grids (8-bit caches)
 };
 
 hipError_t launch_prefill(int dtype, int head_dim, int G, const PrefillArgs& a, hipStream_t s);

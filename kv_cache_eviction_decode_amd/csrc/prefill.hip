@@ -399,7 +399,17 @@ __device__ int block_exclusive_scan(int v, int* sm_wave, int& total) {
   return before + x - v;
 }
 
-template <int DT, int D>
+template <int N> __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&c)[N]) {
+  static_assert(N == 4 || N == 8, "4 or 8 codes");
+  uint32_t w[N / 4];
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i)
+    w[i] = c[4 * i] | c[4 * i + 1] << 8 | c[4 * i + 2] << 16 | c[4 * i + 3] << 24;
+  if constexpr (N == 4) *reinterpret_cast<uint32_t*>(p) = w[0];
+  else *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+}
+
+template <int DT, int D, bool QUANT>
 __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
   constexpr int E = Elem<DT>::bytes, ROW = D * E, LPR = ROW / 16;
   __shared__ int slot_pos[8192];
@@ -497,14 +507,98 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
   const int sub = tid % LPR;
   const char* Kp = static_cast<const char*>(a.K) + size_t(head) * n * ROW + sub * 16;
   const char* Vp = static_cast<const char*>(a.V) + size_t(head) * n * ROW + sub * 16;
-  char* cK = static_cast<char*>(a.cK) + hk * ROW + sub * 16;
-  char* cV = static_cast<char*>(a.cV) + hk * ROW + sub * 16;
-  for (int s = tid / LPR; s < filled; s += kSelThreads / LPR) {
-    const int p = slot_pos[s];
-    if (p < 0 || p >= n) continue;  // cannot happen for a consistent selection
-    const size_t src = size_t(p) * ROW;
-    st16(cK + size_t(s) * ROW, ld16(Kp + src));
-    st16(cV + size_t(s) * ROW, ld16(Vp + src));
+  if constexpr (QUANT) {
+    // 8-bit cache: each lane quantises its EPL elements of the row; keys on
+    // the head's channel grids, values on the row's own grid.
+    constexpr int EPL = 16 / E;
+    const float* kg = a.kq_param + size_t(head) * 2 * D + sub * EPL;
+    float ks[EPL], km[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      ks[e] = kg[e];
+      km[e] = kg[D + e];
+    }
+    uint8_t* cK = static_cast<uint8_t*>(a.cK) + hk * D + sub * EPL;
+    uint8_t* cV = static_cast<uint8_t*>(a.cV) + hk * D + sub * EPL;
+    for (int s = tid / LPR; s < filled; s += kSelThreads / LPR) {
+      const int p = slot_pos[s];
+      if (p < 0 || p >= n) continue;  // cannot happen for a consistent selection
+      const size_t src = size_t(p) * ROW;
+      float x[EPL], v[EPL];
+      Unpack<DT>::run(ld16(Kp + src), x);
+      Unpack<DT>::run(ld16(Vp + src), v);
+      uint32_t kc[EPL], vc[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kc[e] = quantize_u8(x[e], ks[e], km[e]);
+      float vmn = v[0], vmx = v[0];
+#pragma unroll
+      for (int e = 1; e < EPL; ++e) {
+        vmn = fminf(vmn, v[e]);
+        vmx = fmaxf(vmx, v[e]);
+      }
+      vmn = lane_group<LPR>(vmn, OpMin());
+      vmx = lane_group<LPR>(vmx, OpMax());
+      const float vs = u8_grid_scale(vmn, vmx);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vc[e] = quantize_u8(v[e], vs, vmn);
+      store_codes<EPL>(cK + size_t(s) * D, kc);
+      store_codes<EPL>(cV + size_t(s) * D, vc);
+      if (sub == 0) *reinterpret_cast<float2*>(a.vq_param + (hk + s) * 2) = make_float2(vs, vmn);
+    }
+  } else {
+    char* cK = static_cast<char*>(a.cK) + hk * ROW + sub * 16;
+    char* cV = static_cast<char*>(a.cV) + hk * ROW + sub * 16;
+    for (int s = tid / LPR; s < filled; s += kSelThreads / LPR) {
+      const int p = slot_pos[s];
+      if (p < 0 || p >= n) continue;  // cannot happen for a consistent selection
+      const size_t src = size_t(p) * ROW;
+      st16(cK + size_t(s) * ROW, ld16(Kp + src));
+      st16(cV + size_t(s) * ROW, ld16(Vp + src));
+    }
+  }
+}
+
+// Key grids of an 8-bit cache: per (head, channel), the smallest and largest
+// prompt key, scale = (mx - mn) / 255. One workgroup per head.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void key_grid(PrefillArgs a) {
+  constexpr int E = Elem<DT>::bytes, ROW = D * E, LPR = ROW / 16, EPL = 16 / E, RPP = 256 / LPR;
+  __shared__ float sm_mn[RPP][D + 1];
+  __shared__ float sm_mx[RPP][D + 1];
+  const int head = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR, r = tid / LPR;
+  const char* Kp = static_cast<const char*>(a.K) + size_t(head) * a.n * ROW + sub * 16;
+  float mn[EPL], mx[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    mn[e] = __builtin_huge_valf();
+    mx[e] = -__builtin_huge_valf();
+  }
+  for (int j = r; j < a.n; j += RPP) {
+    float x[EPL];
+    Unpack<DT>::run(ld16(Kp + size_t(j) * ROW), x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      mn[e] = fminf(mn[e], x[e]);
+      mx[e] = fmaxf(mx[e], x[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    sm_mn[r][sub * EPL + e] = mn[e];
+    sm_mx[r][sub * EPL + e] = mx[e];
+  }
+  __syncthreads();
+  for (int c = tid; c < D; c += 256) {
+    float lo = sm_mn[0][c], hi = sm_mx[0][c];
+    for (int i = 1; i < RPP; ++i) {
+      lo = fminf(lo, sm_mn[i][c]);
+      hi = fmaxf(hi, sm_mx[i][c]);
+    }
+    float* kg = a.kq_param + size_t(head) * 2 * D;
+    kg[c] = u8_grid_scale(lo, hi);
+    kg[D + c] = lo;
   }
 }
 
@@ -531,7 +625,12 @@ hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((rowlse_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
     hipLaunchKernelGGL((colsum_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
   }
-  hipLaunchKernelGGL((select_gather<DT, D>), dim3(G), dim3(kSelThreads), 0, s, a);
+  if (a.quant) {
+    hipLaunchKernelGGL((key_grid<DT, D>), dim3(G), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((select_gather<DT, D, true>), dim3(G), dim3(kSelThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((select_gather<DT, D, false>), dim3(G), dim3(kSelThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

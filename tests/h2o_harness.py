@@ -11,7 +11,9 @@ either choice is correct).
 Tolerances: attention outputs within max-abs 2e-2 for 16-bit K/V and 1e-4
 for fp32; scores within 1e-4 relative; selected and evicted positions
 bit-exact unless the oracle margin is below 1e-5 relative, in which case the
-GPU's choice must be one of the near-tied correct ones.
+GPU's choice must be one of the near-tied correct ones. For an 8-bit cache
+the codes and the fp32 grids of every cached row are bit-exact too (both
+sides take each rounding decision with the same fp32 operations).
 """
 from __future__ import annotations
 
@@ -64,7 +66,7 @@ def _rel_err(got, ref):
 
 class ParityRun:
     def __init__(self, wl: Workload, steps: int, sample=None, device="cuda", seed=None, policy="accumulated",
-                 split_rows=None):
+                 split_rows=None, quant=None):
         """split_rows: None decodes with h2o_decode_step; an int (0 = the library's
         choice) decodes with h2o_decode_step_split in chunks of that many rows."""
         self.wl = wl
@@ -92,9 +94,10 @@ class ParityRun:
         self.v = to_device(vd.transpose(1, 0, 2), wl.dtype, dev).view(steps, B, H, d)
         del qd, kd, vd
         self.policy = policy
+        self.quant = quant
         self.cache = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, TORCH_DTYPE[wl.dtype], wl.scale, dev,
-                              policy=policy)
-        self.orc = H2OOracle(self.sample.size, d, wl.k_heavy, wl.k_recent, wl.scale, policy)
+                              policy=policy, quant=quant)
+        self.orc = H2OOracle(self.sample.size, d, wl.k_heavy, wl.k_recent, wl.scale, policy, quant=quant)
         self.report = Report()
 
     # -- views of the sampled heads on the GPU
@@ -116,8 +119,27 @@ class ParityRun:
         heads_full = np.asarray(sorted(set(int(h) for h in heads_full)), dtype=np.int64)
         if heads_full.size:
             self._write_sampled(self.cache.pos, self.orc.pos.astype(np.int32), heads_full)
-            self._write_sampled(self.cache.K, self.orc.K.astype(np.float32), heads_full)
-            self._write_sampled(self.cache.V, self.orc.V.astype(np.float32), heads_full)
+            if self.quant:
+                o = self.orc
+                self._write_sampled(self.cache.K, o.Kq, heads_full)
+                self._write_sampled(self.cache.V, o.Vq, heads_full)
+                self._write_sampled(self.cache.v_qparam, np.stack([o.v_scale, o.v_min], -1), heads_full)
+            else:
+                self._write_sampled(self.cache.K, self.orc.K.astype(np.float32), heads_full)
+                self._write_sampled(self.cache.V, self.orc.V.astype(np.float32), heads_full)
+
+    def _check_codes(self, same):
+        """8-bit cache: codes and grids of the heads that agree, bit for bit."""
+        if not self.quant or not same.any():
+            return
+        o = self.orc
+        gK, gV = self._gpu_sampled(self.cache.K), self._gpu_sampled(self.cache.V)
+        gvq = self._gpu_sampled(self.cache.v_qparam)
+        live = (o.pos >= 0)[same]
+        assert np.array_equal(gK[same][live], o.Kq[same][live]), "key codes differ"
+        assert np.array_equal(gV[same][live], o.Vq[same][live]), "value codes differ"
+        assert np.array_equal(gvq[same][live], np.stack([o.v_scale, o.v_min], -1)[same][live]), \
+            "value grids differ"
 
     # -- prefill
     def prefill(self, check_rows=True):
@@ -147,7 +169,11 @@ class ParityRun:
         same = np.array([g not in differ for g in range(self.sample.size)])
         if same.any():
             np.testing.assert_array_less(_rel_err(gscore[same], self.orc.score[same]), SCORE_RTOL * (1 + 1e-9))
-        if check_rows and n:
+        if self.quant:
+            gkq = self._gpu_sampled(self.cache.k_qparam)
+            assert np.array_equal(gkq, np.stack([self.orc.k_scale, self.orc.k_min], 1)), "key grids differ"
+            self._check_codes(same)
+        elif check_rows and n:
             self._check_rows(gpos)
         self.resync(differ)
 
@@ -218,6 +244,7 @@ class ParityRun:
                 rel = _rel_err(gscore[same], self.orc.score[same])
                 rep.max_score_rel = max(rep.max_score_rel, float(rel.max()))
                 assert rel.max() <= SCORE_RTOL, f"step {t}: score rel err {rel.max():.3g}"
+                self._check_codes(same)
             self.resync(differ)
             rep.steps += 1
         return rep

@@ -44,9 +44,10 @@ def test_decode_workspace_bytes():
 
 
 def test_struct_layout_matches_header():
-    # the descriptor is a plain C struct: 8 x 4-byte fields, 4 pointers, 2 int32, int64, 2 uint32
-    assert ctypes.sizeof(b.h2o_cache) == 8 * 4 + 4 * 8 + 2 * 4 + 8 + 2 * 4
+    # the descriptor is a plain C struct: 8 x 4-byte fields, 4 pointers, 2 int32, int64, 2 x 4 bytes, 2 pointers
+    assert ctypes.sizeof(b.h2o_cache) == 8 * 4 + 4 * 8 + 2 * 4 + 8 + 2 * 4 + 2 * 8
     assert b.h2o_cache.K.offset == 32 and b.h2o_cache.steps.offset == 72
+    assert b.h2o_cache.quant.offset == 84 and b.h2o_cache.k_qparam.offset == 88
     assert ctypes.sizeof(b.h2o_state) == 32
 
 
@@ -70,6 +71,14 @@ def test_init_rejects_bad_arguments_without_launching(args, msg):
     assert st == b.H2O_EINVAL
     assert msg in b.h2o_last_error()
     assert d.magic == 0  # descriptor untouched
+
+
+def test_u8_init_rejects_missing_grids():
+    lib = b.load_library()
+    d = b.h2o_cache()
+    st = lib.h2o_cache_init_u8(ctypes.byref(d), 1, 1, 128, 4, 4, 0, 1, 0.1, None, None, None, None, None, None,
+                               None)
+    assert st == b.H2O_EINVAL and "k_qparam" in b.h2o_last_error() and d.magic == 0
 
 
 def test_calls_on_uninitialised_cache_are_rejected():

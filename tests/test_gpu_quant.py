@@ -1,0 +1,65 @@
+"""GPU parity of the 8-bit cache (h2o_cache_init_u8) against the fp64 oracle's
+quantised mode, through the C ABI.
+
+Codes and grids of every cached row are compared bit for bit (both sides
+take each rounding decision with the same fp32 operations); outputs, scores,
+selections and evictions to the same tolerances as the plain cache. Cases
+span both head sizes, every input dtype, ragged prompts, a cache still
+filling, a one-token prompt (degenerate key grids), every policy, a sink
+token, and the OPT-6.7B layer at full size.
+"""
+import zlib
+
+import pytest
+import torch
+
+from h2o_harness import ParityRun, log
+from workload import WORKLOADS, Workload, sample_heads
+
+pytestmark = pytest.mark.gpu
+
+QUANT_CASES = [
+    # name, policy, B, H, d, dtype, n, k_heavy, k_recent, T, sink
+    ("ragged_bf16", "accumulated", 2, 3, 128, "bf16", 300, 20, 20, 60, 0.0),
+    ("f16_d64", "accumulated", 1, 5, 64, "f16", 517, 33, 34, 40, 0.0),
+    ("fills_bf16_d64", "accumulated", 1, 3, 64, "bf16", 20, 24, 24, 50, 0.0),
+    ("f32_d128", "accumulated", 1, 2, 128, "f32", 129, 16, 33, 30, 0.0),
+    ("one_token_prompt", "accumulated", 2, 1, 128, "bf16", 1, 1, 1, 20, 0.0),
+    ("heavy_only", "accumulated", 1, 2, 128, "bf16", 300, 32, 0, 40, 0.0),
+    ("averaged_f16", "averaged", 1, 2, 128, "f16", 200, 24, 24, 40, 0.0),
+    ("position_bf16", "position", 2, 2, 64, "bf16", 333, 4, 28, 40, 0.0),
+    ("sink_f16", "accumulated", 1, 2, 128, "f16", 2048, 205, 205, 16, 4.0),
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
+def test_u8_parity(gpu, case):
+    name, policy, B, H, d, dt, n, kh, kr, T, sink = case
+    wl = Workload("u8_" + name, B, H, d, dt, n, kh, kr, T, 1.5, sink, seed=zlib.crc32(name.encode()) % 10000)
+    run = ParityRun(wl, T, policy=policy, quant="u8")
+    run.prefill()
+    rep = run.decode()
+    log(f"[u8] {name} ({policy}): {rep}")
+    assert rep.steps == T
+
+
+def test_u8_opt_layer_full_size(gpu):
+    """The OPT-6.7B layer shape (2048 heads x 256 slots), as in the benchmark."""
+    wl = WORKLOADS["opt6.7b_layer"]
+    run = ParityRun(wl, 64, sample=sample_heads(wl, 16), quant="u8")
+    run.prefill()
+    rep = run.decode()
+    log(f"[u8] opt6.7b_layer full size: {rep}")
+    assert rep.steps == 64
+
+
+def test_u8_errors(gpu):
+    from kv_cache_eviction_decode_amd import H2OCache, binding as b
+    c = H2OCache(1, 2, 128, 8, 8, torch.bfloat16, device="cuda", quant="u8")
+    z = torch.zeros(1, 2, 0, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(b.H2OError, match="at least one token"):
+        c.prefill_select(z, z, z)
+    q = torch.zeros(1, 2, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(b.H2OError, match="split decode"):
+        c.decode_step_split(q, q, q)
+    assert c.t_next == 0
