@@ -44,13 +44,20 @@ __device__ __forceinline__ uint4 pack_codes(const uint32_t (&c)[16]) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// 16 consecutive elements of a dtype row as fp32.
-template <int DT> __device__ __forceinline__ void load16(const void* row, int first, float (&x)[16]) {
-  constexpr int E = Elem<DT>::bytes, EPC = 16 / E;  // elements per 16-byte chunk
-  const char* p = static_cast<const char*>(row) + size_t(first) * E;
+// 16 consecutive elements of a dtype row: raw 16-byte chunks, then fp32.
+template <int DT> struct Raw16 {
+  static constexpr int E = Elem<DT>::bytes, EPC = 16 / E, N = 16 / EPC;  // chunks of EPC elements
+  uint4 w[N];
+  __device__ __forceinline__ void load(const void* row, int first) {
+    const char* p = static_cast<const char*>(row) + size_t(first) * E;
 #pragma unroll
-  for (int i = 0; i < 16 / EPC; ++i) Unpack<DT>::run(ld16(p + 16 * i), x + EPC * i);
-}
+    for (int i = 0; i < N; ++i) w[i] = ld16(p + 16 * i);
+  }
+  __device__ __forceinline__ void unpack(float (&x)[16]) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) Unpack<DT>::run(w[i], x + EPC * i);
+  }
+};
 
 // One wave per head.
 //   UB: wave-loads of codes (1 KiB of K and 1 KiB of V) per batch; PF: score/pos
@@ -71,17 +78,32 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
   for (int head = blockIdx.x; head < G; head += gridDim.x) {
     const size_t hrow = size_t(head) * a.k;
     // ---- head inputs: q folded with the key grid, the new token, scores ---------------
-    const float* kg = a.k_qparam + size_t(head) * 2 * D + c0;  // this lane's key grids
+    // Everything the epilogue needs is loaded here, so that no load sits on
+    // the head's critical path after the stream.
+    const size_t hoff = size_t(head) * D * Elem<DT>::bytes;
+    Raw16<DT> q_raw, kn_raw, vn_raw;
+    q_raw.load(static_cast<const char*>(a.q) + hoff, c0);
+    kn_raw.load(static_cast<const char*>(a.k_new) + hoff, c0);
+    vn_raw.load(static_cast<const char*>(a.v_new) + hoff, c0);
+    const float4* kg4 = reinterpret_cast<const float4*>(a.k_qparam + size_t(head) * 2 * D + c0);
+    float4 ks4[4], km4[4];  // this lane's key grids
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ks4[i] = kg4[i];
+      km4[i] = kg4[D / 4 + i];
+    }
+    const float* ks = reinterpret_cast<const float*>(ks4);
+    const float* km = reinterpret_cast<const float*>(km4);
     float qs[16];
     float bias;
     {
       float q[16];
-      load16<DT>(static_cast<const char*>(a.q) + size_t(head) * D * Elem<DT>::bytes, c0, q);
+      q_raw.unpack(q);
       float part = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        qs[i] = q[i] * kg[i] * a.c;
-        part = fmaf(q[i], kg[D + i], part);
+        qs[i] = q[i] * ks[i] * a.c;
+        part = fmaf(q[i], km[i], part);
       }
       bias = group_sum<LPR>(part) * a.c;
     }
@@ -125,10 +147,10 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
         const int row = (b * UB + j) * RPU + grp;
         float c[16];
         codes_to_float(kb[j], c);
-        float x = 0.f;
+        float x4[4] = {0.f, 0.f, 0.f, 0.f};  // four short chains instead of one long one
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x = fmaf(qs[i], c[i], x);
-        x = group_sum<LPR>(x) + bias;
+        for (int i = 0; i < 16; ++i) x4[i % 4] = fmaf(qs[i], c[i], x4[i % 4]);
+        const float x = group_sum<LPR>((x4[0] + x4[1]) + (x4[2] + x4[3])) + bias;
         s[j] = row < nu ? x : kNegInf;
         bm = fmaxf(bm, s[j]);
         if (sub == 0 && row < nu) sm_logit[row] = s[j];
@@ -169,9 +191,9 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
 
     // ---- merge the lane groups, output -------------------------------------------------
     float qf[16], kn[16], vn[16];
-    load16<DT>(static_cast<const char*>(a.q) + size_t(head) * D * Elem<DT>::bytes, c0, qf);
-    load16<DT>(static_cast<const char*>(a.k_new) + size_t(head) * D * Elem<DT>::bytes, c0, kn);
-    load16<DT>(static_cast<const char*>(a.v_new) + size_t(head) * D * Elem<DT>::bytes, c0, vn);
+    q_raw.unpack(qf);
+    kn_raw.unpack(kn);
+    vn_raw.unpack(vn);
     float sn = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sn = fmaf(qf[i], kn[i], sn);
@@ -276,7 +298,7 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
         uint32_t kc[16], vc[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          kc[i] = quantize_u8(kn[i], kg[i], kg[D + i]);
+          kc[i] = quantize_u8(kn[i], ks[i], km[i]);
           vc[i] = quantize_u8(vn[i], vs, vmn);
         }
         st16(static_cast<uint8_t*>(a.K_w) + (hrow + victim) * D + c0, pack_codes(kc));
@@ -290,7 +312,7 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
 
 template <int DT, int D>
 hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
-  constexpr int UB = 4, PF = 4, MINW = 2;
+  constexpr int UB = 2, PF = 4, MINW = 2;
   const int resident = cu_count() * 4 * MINW;
   const int grid = G < resident ? G : resident;
   const size_t shmem = size_t(a.k) * sizeof(float);
