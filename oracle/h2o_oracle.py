@@ -74,7 +74,7 @@ import numpy as np
 
 from . import quant as qz
 
-__all__ = ["causal_attention_probs", "prefill_column_sums", "select_prefill", "retention_value",
+__all__ = ["causal_attention_probs", "prefill_column_sums", "prefill_attention", "select_prefill", "retention_value",
            "eligible_slots", "choose_victim", "H2OOracle", "PrefillResult", "StepResult", "POLICIES"]
 
 POLICIES = ("accumulated", "averaged", "position")
@@ -112,6 +112,24 @@ def causal_attention_probs(Q: np.ndarray, K: np.ndarray, scale: float) -> np.nda
     S = np.where(np.tril(np.ones((n, n), dtype=bool)), S, -np.inf)
     E = np.exp(S - S.max(axis=1, keepdims=True))
     return E / E.sum(axis=1, keepdims=True)
+
+
+def prefill_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """The prompt's own causal attention: output rows O_i = sum_j P[i, j] V_j
+    and each row's log normaliser lse_i = log sum_{j <= i} exp(scale <Q_i, K_j>)
+    (natural log), H2O §D "Recursive attention" (o_i and D_i)."""
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    n = Q.shape[0]
+    if n == 0:
+        return np.zeros((0, V.shape[1])), np.zeros(0)
+    S = scale * (Q @ K.T)
+    S = np.where(np.tril(np.ones((n, n), dtype=bool)), S, -np.inf)
+    mx = S.max(axis=1, keepdims=True)
+    E = np.exp(S - mx)
+    Z = E.sum(axis=1, keepdims=True)
+    return (E / Z) @ V, (mx + np.log(Z))[:, 0]
 
 
 def prefill_column_sums(Q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:

@@ -379,3 +379,23 @@ def test_averaged_value_counts_queries():
     avg = c[:n - 5] / (n - np.arange(n - 5))
     expect = sorted(np.argsort(-avg, kind="stable")[:5].tolist())
     assert keep[:5].tolist() == expect
+
+
+def test_prefill_attention_is_causal_sdpa():
+    """The prompt's attention output and row normalisers against torch's
+    scaled_dot_product_attention (float64, causal) and a log-sum-exp written
+    out with torch; q = 0 gives running means of V and lse_i = log(i + 1)."""
+    from oracle.h2o_oracle import prefill_attention
+    rng = np.random.default_rng(21)
+    n, d, scale = 37, 16, 0.31
+    Q, K, V = (rng.standard_normal((n, d)) for _ in range(3))
+    O, lse = prefill_attention(Q, K, V, scale)
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (Q, K, V))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)[0, 0].numpy()
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+    s = scale * torch.from_numpy(Q) @ torch.from_numpy(K).T
+    s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=1).numpy(), rtol=0, atol=1e-12)
+    O0, lse0 = prefill_attention(np.zeros((n, d)), K, V, scale)
+    np.testing.assert_allclose(O0, np.cumsum(V, 0) / np.arange(1, n + 1)[:, None], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse0, np.log(np.arange(1, n + 1)), rtol=0, atol=1e-12)
