@@ -385,6 +385,8 @@ def test_prefill_attention_is_causal_sdpa():
     """The prompt's attention output and row normalisers against torch's
     scaled_dot_product_attention (float64, causal) and a log-sum-exp written
     out with torch; q = 0 gives running means of V and lse_i = log(i + 1)."""
+    import torch
+
     from oracle.h2o_oracle import prefill_attention
     rng = np.random.default_rng(21)
     n, d, scale = 37, 16, 0.31
