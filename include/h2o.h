@@ -179,6 +179,34 @@ h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, c
                               float* colsum_out, h2o_stream_t stream);
 
 /*
+ * h2o_prefill_select that also returns the prompt's own causal attention
+ * (H2O §D "Recursive attention": o_i = sum_{j<=i} softmax_j(scale*q_i.k_j) v_j
+ * with its normaliser D_i), so that a model's prefill attention and the H2O
+ * scoring share the first QK^T pass and H2O's extra cost is the column-sum
+ * pass alone:
+ *   out     : [batch][heads][n][head_dim] fp32, o_i (required when n > 0)
+ *   lse_out : optional [batch][heads][n] fp32, log sum_{j<=i} exp(scale*q_i.k_j)
+ *             (natural log), or NULL
+ * Everything else as for h2o_prefill_select.
+ */
+h2o_status h2o_prefill_attention(h2o_cache* cache, const void* Q, const void* Kp, const void* Vp,
+                                 int32_t n, void* workspace, size_t workspace_bytes, float* out,
+                                 float* lse_out, float* colsum_out, h2o_stream_t stream);
+
+/*
+ * h2o_prefill_select for a caller whose own attention kernel already produced
+ * each prompt row's log normaliser:
+ *   lse : [batch][heads][n] fp32 device, log sum_{j<=i} exp(scale*q_i.k_j)
+ *         (natural log, the cache's scale), e.g. the log-sum-exp a fused
+ *         attention forward emits.
+ * Only the column-sum pass forms QK^T; its terms are exp(scale*q_i.k_j - lse_i),
+ * so the column sums are exact for the normalisers given.
+ */
+h2o_status h2o_prefill_select_lse(h2o_cache* cache, const void* Q, const void* Kp, const void* Vp,
+                                  int32_t n, const float* lse, void* workspace, size_t workspace_bytes,
+                                  float* colsum_out, h2o_stream_t stream);
+
+/*
  * One decode step at position t = t_next for every (b,h) (H2O §D "Recursive
  * attention" then "Cache eviction"; H2O §2 "Problem formulation"):
  *   q, k_new, v_new : [batch][heads][head_dim] dtype, the new token

@@ -80,6 +80,10 @@ _SIGNATURES = {
                                _P, _P, _P, _P, _P, _P, _P]),
     "h2o_prefill_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "h2o_prefill_select": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _I, _P, ctypes.c_size_t, _P, _P]),
+    "h2o_prefill_attention": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _I, _P, ctypes.c_size_t, _P, _P, _P,
+                                   _P]),
+    "h2o_prefill_select_lse": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _I, _P, _P, ctypes.c_size_t, _P,
+                                    _P]),
     "h2o_decode_step": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _P, _P, _P]),
     "h2o_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "h2o_decode_step_split": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
@@ -204,6 +208,40 @@ def h2o_prefill_select(desc: h2o_cache, Q, K, V, workspace: torch.Tensor | None,
         _expect(colsum_out, "colsum_out", (B, H, n), torch.float32, device)
     _check(load_library().h2o_prefill_select(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), n, ws_ptr,
                                              ws_bytes, _ptr(colsum_out), _stream_handle(stream)))
+
+
+def _prompt_args(desc, Q, K, V, workspace, colsum_out, device):
+    B, H, d = desc.batch, desc.heads, desc.head_dim
+    n = Q.shape[2]
+    dt = _desc_dtype(desc)
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        _expect(t, name, (B, H, n, d), dt, device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _expect(workspace, "workspace", (workspace.numel(),), torch.uint8, device)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
+    if colsum_out is not None:
+        _expect(colsum_out, "colsum_out", (B, H, n), torch.float32, device)
+    return n, ws_ptr, ws_bytes
+
+
+def h2o_prefill_attention(desc: h2o_cache, Q, K, V, workspace, out, lse_out=None, colsum_out=None, stream=None,
+                          device=None):
+    n, ws_ptr, ws_bytes = _prompt_args(desc, Q, K, V, workspace, colsum_out, device)
+    shape = (desc.batch, desc.heads, n)
+    _expect(out, "out", shape + (desc.head_dim,), torch.float32, device)
+    if lse_out is not None:
+        _expect(lse_out, "lse_out", shape, torch.float32, device)
+    _check(load_library().h2o_prefill_attention(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), n, ws_ptr,
+                                                ws_bytes, _ptr(out), _ptr(lse_out), _ptr(colsum_out),
+                                                _stream_handle(stream)))
+
+
+def h2o_prefill_select_lse(desc: h2o_cache, Q, K, V, lse, workspace, colsum_out=None, stream=None, device=None):
+    n, ws_ptr, ws_bytes = _prompt_args(desc, Q, K, V, workspace, colsum_out, device)
+    _expect(lse, "lse", (desc.batch, desc.heads, n), torch.float32, device)
+    _check(load_library().h2o_prefill_select_lse(ctypes.byref(desc), _ptr(Q), _ptr(K), _ptr(V), n, _ptr(lse),
+                                                 ws_ptr, ws_bytes, _ptr(colsum_out), _stream_handle(stream)))
 
 
 def h2o_decode_step(desc: h2o_cache, q, k_new, v_new, out, evicted, stream=None, device=None):
@@ -332,6 +370,22 @@ class H2OCache:
         n = Q.shape[2]
         ws = self.workspace(n) if n > 0 else None
         h2o_prefill_select(self.desc, Q, K, V, ws, colsum_out, stream, self.device)
+
+    def prefill_attention(self, Q, K, V, out=None, lse_out=None, colsum_out=None, stream=None):
+        """Prefill that also returns the prompt's attention output [B, H, n, d] (fp32)."""
+        n = Q.shape[2]
+        if out is None:
+            out = torch.empty(self.batch, self.heads, n, self.desc.head_dim, dtype=torch.float32,
+                              device=self.device)
+        ws = self.workspace(n) if n > 0 else None
+        h2o_prefill_attention(self.desc, Q, K, V, ws, out, lse_out, colsum_out, stream, self.device)
+        return out
+
+    def prefill_select_lse(self, Q, K, V, lse, colsum_out=None, stream=None):
+        """Prefill scoring with the prompt rows' log normalisers given (natural log)."""
+        n = Q.shape[2]
+        ws = self.workspace(n) if n > 0 else None
+        h2o_prefill_select_lse(self.desc, Q, K, V, lse, ws, colsum_out, stream, self.device)
 
     def decode_step(self, q, k_new, v_new, out=None, evicted=None, stream=None):
         if out is None:

@@ -94,39 +94,9 @@ h2o_status init_cache(h2o_cache* cache, int32_t batch, int32_t heads, int32_t he
   return H2O_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* h2o_last_error(void) { return g_err; }
-
-h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
-                          int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
-                          void* K, void* V, float* score, int32_t* pos, h2o_stream_t stream) {
-  return init_cache(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, K, V, score, pos,
-                    H2O_QUANT_NONE, nullptr, nullptr, stream);
-}
-
-h2o_status h2o_cache_init_u8(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
-                             int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
-                             uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam, float* score,
-                             int32_t* pos, h2o_stream_t stream) {
-  if (!k_qparam || !v_qparam) return fail(H2O_EINVAL, "k_qparam and v_qparam must be non-NULL");
-  if (!aligned(k_qparam, 16) || !aligned(v_qparam, 16))
-    return fail(H2O_EINVAL, "k_qparam and v_qparam must be 16-byte aligned");
-  return init_cache(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, Kq, Vq, score, pos,
-                    H2O_QUANT_U8, k_qparam, v_qparam, stream);
-}
-
-size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n) {
-  if (batch < 1 || heads < 1 || n < 0) return 0;
-  const size_t G = size_t(batch) * heads;
-  return align256(G * lse_ld(n) * sizeof(float)) + align256(G * size_t(n) * sizeof(float));
-}
-
-h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, const void* Vp,
-                              int32_t n, void* workspace, size_t workspace_bytes, float* colsum_out,
-                              h2o_stream_t stream) {
+h2o_status prefill(h2o_cache* cache, const void* Q, const void* Kp, const void* Vp, int32_t n, void* workspace,
+                   size_t workspace_bytes, float* colsum_out, int32_t pass1, float* out, float* lse_out,
+                   const float* lse_in, h2o_stream_t stream, const char* who) {
   h2o_status st = check_cache(cache);
   if (st != H2O_OK) return st;
   if (cache->t_next != 0) return fail(H2O_ESTATE, "prefill needs a freshly initialised cache (t_next = %d)", cache->t_next);
@@ -164,13 +134,73 @@ h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, c
   a.quant = cache->quant;
   a.kq_param = cache->k_qparam;
   a.vq_param = cache->v_qparam;
+  a.pass1 = pass1;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.lse_in = lse_in;
   st = device_status(h2o::launch_prefill(cache->dtype, cache->head_dim, G, a, static_cast<hipStream_t>(stream)),
-                     "h2o_prefill_select");
+                     who);
   if (st != H2O_OK) return st;
   const int32_t k = cache->k_heavy + cache->k_recent;
   cache->t_next = n;
   cache->n_used = n < k ? n : k;
   return H2O_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* h2o_last_error(void) { return g_err; }
+
+h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                          int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
+                          void* K, void* V, float* score, int32_t* pos, h2o_stream_t stream) {
+  return init_cache(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, K, V, score, pos,
+                    H2O_QUANT_NONE, nullptr, nullptr, stream);
+}
+
+h2o_status h2o_cache_init_u8(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                             int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
+                             uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam, float* score,
+                             int32_t* pos, h2o_stream_t stream) {
+  if (!k_qparam || !v_qparam) return fail(H2O_EINVAL, "k_qparam and v_qparam must be non-NULL");
+  if (!aligned(k_qparam, 16) || !aligned(v_qparam, 16))
+    return fail(H2O_EINVAL, "k_qparam and v_qparam must be 16-byte aligned");
+  return init_cache(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, Kq, Vq, score, pos,
+                    H2O_QUANT_U8, k_qparam, v_qparam, stream);
+}
+
+size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n) {
+  if (batch < 1 || heads < 1 || n < 0) return 0;
+  const size_t G = size_t(batch) * heads;
+  return align256(G * lse_ld(n) * sizeof(float)) + align256(G * size_t(n) * sizeof(float));
+}
+
+h2o_status h2o_prefill_select(h2o_cache* cache, const void* Q, const void* Kp, const void* Vp,
+                              int32_t n, void* workspace, size_t workspace_bytes, float* colsum_out,
+                              h2o_stream_t stream) {
+  return prefill(cache, Q, Kp, Vp, n, workspace, workspace_bytes, colsum_out, h2o::PASS1_LSE, nullptr, nullptr,
+                 nullptr, stream, "h2o_prefill_select");
+}
+
+h2o_status h2o_prefill_attention(h2o_cache* cache, const void* Q, const void* Kp, const void* Vp, int32_t n,
+                                 void* workspace, size_t workspace_bytes, float* out, float* lse_out,
+                                 float* colsum_out, h2o_stream_t stream) {
+  if (n > 0 && !out) return fail(H2O_EINVAL, "out must be non-NULL");
+  if (out && !aligned(out, 16)) return fail(H2O_EINVAL, "out must be 16-byte aligned");
+  if (lse_out && !aligned(lse_out, 4)) return fail(H2O_EINVAL, "lse_out must be 4-byte aligned");
+  return prefill(cache, Q, Kp, Vp, n, workspace, workspace_bytes, colsum_out, h2o::PASS1_ATTENTION, out, lse_out,
+                 nullptr, stream, "h2o_prefill_attention");
+}
+
+h2o_status h2o_prefill_select_lse(h2o_cache* cache, const void* Q, const void* Kp, const void* Vp, int32_t n,
+                                  const float* lse, void* workspace, size_t workspace_bytes, float* colsum_out,
+                                  h2o_stream_t stream) {
+  if (n > 0 && !lse) return fail(H2O_EINVAL, "lse must be non-NULL");
+  if (lse && !aligned(lse, 4)) return fail(H2O_EINVAL, "lse must be 4-byte aligned");
+  return prefill(cache, Q, Kp, Vp, n, workspace, workspace_bytes, colsum_out, h2o::PASS1_GIVEN, nullptr, nullptr,
+                 lse, stream, "h2o_prefill_select_lse");
 }
 
 h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,

@@ -80,7 +80,15 @@ struct PrefillArgs {
   int32_t quant;   // h2o_quant of the cache
   float* kq_param; // [G][2][d] key grids (8-bit caches)
   float* vq_param; // [G][k][2] value grids (8-bit caches)
+  int32_t pass1;   // PASS1_* below: how the row normalisers are obtained
+  float* out;      // [G][n][d] fp32 prompt attention output (PASS1_ATTENTION)
+  float* lse_out;  // [G][n] natural-log row normalisers, optional (PASS1_ATTENTION)
+  const float* lse_in;  // [G][n] natural-log row normalisers given by the caller (PASS1_GIVEN)
 };
+
+// Pass 1 of the prefill: row normalisers only, normalisers together with the
+// prompt's attention output, or normalisers handed in by the caller.
+enum : int32_t { PASS1_LSE = 0, PASS1_ATTENTION = 1, PASS1_GIVEN = 2 };
 
 hipError_t launch_prefill(int dtype, int head_dim, int G, const PrefillArgs& a, hipStream_t s);
 

@@ -210,6 +210,201 @@ __global__ __launch_bounds__(256, 2) void rowlse_lds(PrefillArgs a, int nblk, in
   }
 }
 
+// ---------------------------------------------------------------- pass 1 with output
+// The V tile of 64 keys is staged transposed in LDS for the P.V product:
+// channel row r holds the 64 keys' values of channel r. Within a row, groups
+// of 4 keys are permuted by XOR with the row's 8-channel chunk index, which
+// spreads the transposing 2-byte writes of one source row over distinct banks
+// while keeping every 4-key group contiguous for the 8-byte fragment reads.
+template <int DT, int D>
+struct VTileT {
+  using T = Tile64<DT, D>;
+  static constexpr int RS = 64 * 2 + 8;  // bytes per channel row (16-bit types), padded
+  static constexpr int BYTES = D * RS;
+  __device__ __forceinline__ static int phys(int key, int ch) { return key ^ ((ch & 15) << 2); }
+  __device__ __forceinline__ static void store(char* lds, const uint4 (&r)[T::CPT]) {
+#pragma unroll
+    for (int i = 0; i < T::CPT; ++i) {
+      const int key = T::my_row(i), ch = T::my_chunk();
+      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(lds + (ch * 8 + e) * RS + phys(key, ch) * 2) =
+            uint16_t(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+  // A operand of the P.V MFMA: channel row d, keys key0 .. key0+3 and key0+8 .. key0+11.
+  __device__ __forceinline__ static uint4 frag(const char* lds, int d, int key0) {
+    const char* row = lds + d * RS;
+    const uint2 lo = *reinterpret_cast<const uint2*>(row + phys(key0, d >> 3) * 2);
+    const uint2 hi = *reinterpret_cast<const uint2*>(row + phys(key0 + 8, d >> 3) * 2);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+};
+
+// Eight probabilities as one 16-byte MFMA operand of the input type.
+template <int DT> __device__ __forceinline__ uint4 pack8(const float* p);
+template <> __device__ __forceinline__ uint4 pack8<DT_BF16>(const float* p) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)p[i];
+  return __builtin_bit_cast(uint4, v);
+}
+template <> __device__ __forceinline__ uint4 pack8<DT_F16>(const float* p) {
+  f16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (_Float16)p[i];
+  return __builtin_bit_cast(uint4, v);
+}
+
+// Pass 1 emitting the prompt's own attention output O = P V as well as
+// lse2 (H2O §D "Recursive attention": o_i together with its normaliser D_i).
+// The S^T tiles are those of rowlse_lds; the probabilities of a 16-key group
+// held by a lane are exactly the 8 k values the lane supplies as the B
+// operand of O^T = V^T P^T (k slot 8h+i <-> key 16g + 8(i/4) + 4h + i%4), so P
+// never leaves registers; V^T comes from the transposed LDS tile. The online
+// softmax keeps one running maximum per query column, shared by both lane
+// halves, and rescales the O accumulators when it grows.
+template <int DT, int D>
+__global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
+  using T = Tile64<DT, D>;
+  using VT = VTileT<DT, D>;
+  constexpr int NDB = D / 32;  // 32-channel blocks of the output
+  __shared__ __attribute__((aligned(16))) char lds_k[2][T::BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_v[2][VT::BYTES];
+  const int L = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (L >= G * nblk) return;  // uniform over the workgroup
+  const int head = L / nblk;
+  const int qb = nblk - 1 - L % nblk;  // longest causal extent first
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lh = lane >> 5;
+  const int n = a.n;
+  const int wg_q0 = qb * 256;
+  const int q0 = wg_q0 + wave * 64;
+  const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
+  const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
+  const char* Vh = static_cast<const char*>(a.V) + size_t(head) * n * T::ROW;
+  const float c = a.c;
+
+  uint4 qf[2][T::KS];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = min(q0 + cb * 32 + (lane & 31), n - 1);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
+  }
+  wait_vmem_all();
+  f32x16 o[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db][0] = o[db][1] = f32x16{};
+  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+  const int ntiles = min(wg_q0 + 255, n - 1) / 64 + 1;
+  uint4 nk[T::CPT], nv[T::CPT];
+  T::fetch(nk, Kh, 0, n);
+  T::fetch(nv, Vh, 0, n);
+  T::store(lds_k[0], nk);
+  VT::store(lds_v[0], nv);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    if (kt + 1 < ntiles) {
+      T::fetch(nk, Kh, (kt + 1) * 64, n);
+      T::fetch(nv, Vh, (kt + 1) * 64, n);
+    }
+    const char* kbuf = lds_k[kt & 1];
+    const char* vbuf = lds_v[kt & 1];
+    const int key0 = kt * 64;
+    if (key0 <= min(q0 + 63, n - 1)) {  // every query of this wave sees key0
+      f32x16 acc[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        uint4 af[T::KS];
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(kbuf, kb, ks, lane);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          acc[kb][cb] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < T::KS; ++ks) acc[kb][cb] = MfmaOp<DT>::run(af[ks], qf[cb][ks], acc[kb][cb]);
+        }
+      }
+      // acc[kb][cb][j] = s(query q0 + 32cb + lane%32, key key0 + 32kb + mfma_row(j))
+      uint4 pb[2][2][2];  // [cb][kb][g]: B operands of the P.V product
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int qi = q0 + cb * 32 + (lane & 31);
+        if (key0 + 63 > q0 + cb * 32) {  // tile reaches past some query of this block: mask
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][cb][j] = kNegInf;
+        }
+        float tm = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][cb][j], acc[0][cb][j + 1]);
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
+        const float mn = fmaxf(m[cb], fmaxf(tm, __shfl_xor(tm, 32)));  // same in both halves
+        const float mnc = mn * c;
+        const float alpha = fast_exp2((m[cb] - mn) * c);
+        float t = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float p[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            p[j] = fast_exp2(fmaf(acc[kb][cb][j], c, -mnc));
+            t += p[j];
+          }
+          pb[cb][kb][0] = pack8<DT>(p);
+          pb[cb][kb][1] = pack8<DT>(p + 8);
+        }
+        l[cb] = fmaf(l[cb], alpha, t);
+        m[cb] = mn;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db][cb] *= alpha;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const uint4 vf = VT::frag(vbuf, db * 32 + (lane & 31), kb * 32 + g * 16 + lh * 4);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) o[db][cb] = MfmaOp<DT>::run(vf, pb[cb][kb][g], o[db][cb]);
+          }
+    }
+    if (kt + 1 < ntiles) {
+      T::store(lds_k[(kt + 1) & 1], nk);
+      VT::store(lds_v[(kt + 1) & 1], nv);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float lt = l[cb] + __shfl_xor(l[cb], 32);  // both halves share the maximum
+    const int qi = q0 + cb * 32 + (lane & 31);
+    if (qi < n) {
+      const float lse2 = m[cb] * c + fast_log2(lt);
+      if (lh == 0) {
+        a.lse2[size_t(head) * ld_lse + qi] = lse2;
+        if (a.lse_out) a.lse_out[size_t(head) * n + qi] = lse2 * 0.6931471805599453f;
+      }
+      const float inv = 1.0f / lt;
+      float* orow = a.out + (size_t(head) * n + qi) * D;
+      // o[db][cb][j] = O(query qi, channel 32db + mfma_row(j))
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<float4*>(orow + db * 32 + 8 * jj + 4 * lh) =
+              make_float4(o[db][cb][4 * jj] * inv, o[db][cb][4 * jj + 1] * inv, o[db][cb][4 * jj + 2] * inv,
+                          o[db][cb][4 * jj + 3] * inv);
+    }
+  }
+}
+
 // Pass 2: c_j = sum_{i>=j} 2^(c*s_ij - lse2_i). Workgroup = 256 keys (64 per
 // wave, held in registers as MFMA B operands); queries streamed in 64-row LDS
 // tiles together with their lse2. Each lane owns one key column; the tile
@@ -349,6 +544,49 @@ __global__ __launch_bounds__(256) void rowlse_valu(PrefillArgs a, int nblk, int 
     m = mn;
   }
   a.lse2[size_t(head) * ld_lse + i] = m * c + fast_log2(l);
+}
+
+// Pass 1 with output, fp32: one thread per query, its output row in registers.
+template <int D>
+__global__ __launch_bounds__(256) void rowattn_valu(PrefillArgs a, int nblk, int ld_lse) {
+  const int head = blockIdx.x / nblk;
+  const int i = (blockIdx.x % nblk) * 256 + threadIdx.x;
+  const int n = a.n;
+  if (i >= n) return;
+  const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
+  const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
+  const float* V = static_cast<const float*>(a.V) + size_t(head) * n * D;
+  const float c = a.c;
+  float m = kNegInf, l = 0.f;
+  float o[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) o[e] = 0.f;
+  for (int j = 0; j <= i; ++j) {
+    float s = 0.f;
+    for (int e = 0; e < D; ++e) s = fmaf(Q[size_t(i) * D + e], K[size_t(j) * D + e], s);
+    const float mn = fmaxf(m, s);
+    const float alpha = fast_exp2((m - mn) * c), p = fast_exp2((s - mn) * c);
+    l = fmaf(l, alpha, p);
+#pragma unroll
+    for (int e = 0; e < D; ++e) o[e] = fmaf(o[e], alpha, p * V[size_t(j) * D + e]);
+    m = mn;
+  }
+  const float lse2 = m * c + fast_log2(l);
+  a.lse2[size_t(head) * ld_lse + i] = lse2;
+  if (a.lse_out) a.lse_out[size_t(head) * n + i] = lse2 * 0.6931471805599453f;
+  const float inv = 1.0f / l;
+  float* orow = a.out + (size_t(head) * n + i) * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) orow[e] = o[e] * inv;
+}
+
+// Pass 1 replaced by the caller's natural-log normalisers: lse2 = lse * log2(e).
+__global__ void lse_from_natural(PrefillArgs a, int G, int ld_lse) {
+  const int64_t total = int64_t(G) * a.n;
+  for (int64_t x = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; x < total; x += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t g = x / a.n, i = x % a.n;
+    a.lse2[g * ld_lse + i] = a.lse_in[x] * kLog2e;
+  }
 }
 
 template <int D>
@@ -615,14 +853,24 @@ int pad8(int x) { return (x + 7) & ~7; }
 template <int DT, int D>
 hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
   const int ld_lse = (a.n + 63) & ~63;
+  const int nblk = (a.n + 255) / 256;
+  if (a.pass1 == PASS1_GIVEN) {
+    int64_t blocks = (int64_t(G) * a.n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(lse_from_natural, dim3(unsigned(blocks)), dim3(256), 0, s, a, G, ld_lse);
+  }
   if constexpr (DT == DT_F32) {
-    const int nblk = (a.n + 255) / 256;
-    hipLaunchKernelGGL((rowlse_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
+    if (a.pass1 == PASS1_LSE)
+      hipLaunchKernelGGL((rowlse_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
+    else if (a.pass1 == PASS1_ATTENTION)
+      hipLaunchKernelGGL((rowattn_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
     hipLaunchKernelGGL((colsum_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
   } else {
-    const int nblk = (a.n + 255) / 256;
     const int grid = pad8(G * nblk);
-    hipLaunchKernelGGL((rowlse_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
+    if (a.pass1 == PASS1_LSE)
+      hipLaunchKernelGGL((rowlse_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
+    else if (a.pass1 == PASS1_ATTENTION)
+      hipLaunchKernelGGL((rowattn_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
     hipLaunchKernelGGL((colsum_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
   }
   if (a.quant) {

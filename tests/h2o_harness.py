@@ -25,7 +25,7 @@ import torch
 
 from kv_cache_eviction_decode_amd import H2OCache
 from oracle import H2OOracle
-from oracle.h2o_oracle import retention_value
+from oracle.h2o_oracle import prefill_attention, retention_value
 from workload import Workload, make_decode, make_prompt
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -54,6 +54,8 @@ class Report:
     max_out_err: float = 0.0
     max_score_rel: float = 0.0
     max_colsum_rel: float = 0.0
+    max_prompt_out_err: float = 0.0
+    max_lse_err: float = 0.0
     excused_selections: int = 0
     excused_evictions: int = 0
     evictions_checked: int = 0
@@ -142,13 +144,40 @@ class ParityRun:
             "value grids differ"
 
     # -- prefill
-    def prefill(self, check_rows=True):
+    def prefill(self, check_rows=True, mode="select"):
+        """mode: "select" (h2o_prefill_select), "attention" (h2o_prefill_attention,
+        whose prompt output and log normalisers are checked too) or "lse"
+        (h2o_prefill_select_lse fed with the oracle's normalisers)."""
         wl, rep = self.wl, self.report
         n = wl.prompt_len
         colsum = torch.empty(wl.batch, wl.heads, n, dtype=torch.float32, device=self.device) if n else None
-        self.cache.prefill_select(self.Q, self.K, self.V, colsum_out=colsum)
+        ref = None
+        if mode != "select":
+            ref = [prefill_attention(self.oQ[g], self.oK[g], self.oV[g], wl.scale) for g in range(self.sample.size)]
+        if mode == "attention":
+            lse = torch.empty(wl.batch, wl.heads, n, dtype=torch.float32, device=self.device)
+            out = self.cache.prefill_attention(self.Q, self.K, self.V, lse_out=lse, colsum_out=colsum)
+        elif mode == "lse":
+            assert self.sample.size == wl.n_heads_total, "the oracle supplies every head's normalisers"
+            lse_h = np.zeros((wl.n_heads_total, n), np.float32)
+            if n:
+                lse_h[self.sample] = np.stack([r[1] for r in ref])
+            lse = torch.from_numpy(lse_h).to(self.device).view(wl.batch, wl.heads, n)
+            self.cache.prefill_select_lse(self.Q, self.K, self.V, lse, colsum_out=colsum)
+        else:
+            self.cache.prefill_select(self.Q, self.K, self.V, colsum_out=colsum)
         pre = self.orc.prefill(self.oQ, self.oK, self.oV)
         torch.cuda.synchronize()
+        if mode == "attention" and n:
+            gout = self._gpu_sampled(out)
+            glse = self._gpu_sampled(lse)
+            for g in range(self.sample.size):
+                err = float(np.abs(gout[g] - ref[g][0]).max())
+                rep.max_prompt_out_err = max(rep.max_prompt_out_err, err)
+                assert err <= out_tolerance(wl.dtype), f"head {self.sample[g]}: prompt output err {err:.3g}"
+                lerr = float(np.abs(glse[g] - ref[g][1]).max())
+                rep.max_lse_err = max(rep.max_lse_err, lerr)
+                assert lerr <= 1e-4 * max(1.0, float(np.abs(ref[g][1]).max())), f"lse err {lerr:.3g}"
         assert self.cache.n_used == self.orc.n_used and self.cache.t_next == self.orc.t == n
         gpos = self._gpu_sampled(self.cache.pos)
         gscore = self._gpu_sampled(self.cache.score)

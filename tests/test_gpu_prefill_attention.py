@@ -1,0 +1,61 @@
+"""GPU parity of the prefill entry points that share pass 1 with the model's
+own prompt attention (h2o_prefill_attention) or take its normalisers
+(h2o_prefill_select_lse), against the fp64 oracle, through the C ABI.
+
+The prompt's attention output is compared element by element (max-abs 2e-2
+for 16-bit inputs, 1e-4 for fp32) and its log normalisers to 1e-4 relative;
+the column sums, the selection and the decode steps that follow must meet the
+same bar as after h2o_prefill_select. Prompts span several 64-key tiles and
+256-query blocks with ragged tails, a single token, exactly one tile, both
+head sizes and every input dtype; the named workloads run at full size with
+sampled heads.
+"""
+import zlib
+
+import pytest
+
+from h2o_harness import ParityRun, log
+from workload import WORKLOADS, Workload, sample_heads
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, B, H, d, dtype, n, k_heavy, k_recent, T
+    ("ragged_bf16_d128", 2, 3, 128, "bf16", 300, 20, 20, 20),
+    ("ragged_f16_d64", 1, 5, 64, "f16", 517, 33, 34, 20),
+    ("f32_d128", 1, 2, 128, "f32", 129, 16, 33, 10),
+    ("f32_d64", 2, 1, 64, "f32", 70, 8, 8, 10),
+    ("one_token_bf16", 2, 1, 128, "bf16", 1, 1, 1, 10),
+    ("one_tile_f16", 1, 2, 128, "f16", 64, 12, 12, 10),
+    ("two_blocks_bf16_d64", 1, 2, 64, "bf16", 600, 40, 40, 10),
+]
+
+
+@pytest.mark.parametrize("mode", ["attention", "lse"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_modes_parity(gpu, case, mode):
+    name, B, H, d, dt, n, kh, kr, T = case
+    wl = Workload(name, B, H, d, dt, n, kh, kr, T, 1.5, 0.0, seed=zlib.crc32(name.encode()) % 10000)
+    run = ParityRun(wl, T)
+    run.prefill(mode=mode)
+    rep = run.decode()
+    log(f"[prefill {mode}] {name}: {rep}")
+    assert rep.steps == T
+
+
+def test_prefill_attention_u8_cache(gpu):
+    wl = Workload("attn_u8", 1, 3, 128, "bf16", 333, 24, 24, 20, 1.5, 0.0, seed=77)
+    run = ParityRun(wl, wl.steps, quant="u8")
+    run.prefill(mode="attention")
+    rep = run.decode()
+    log(f"[prefill attention] u8 cache: {rep}")
+
+
+@pytest.mark.parametrize("name,nsample", [("opt6.7b_layer", 8), ("opt30b_layer", 4), ("long_context", 2)])
+def test_prefill_attention_full_size(gpu, name, nsample):
+    wl = WORKLOADS[name]
+    run = ParityRun(wl, 8, sample=sample_heads(wl, nsample))
+    run.prefill(mode="attention")
+    rep = run.decode()
+    log(f"[prefill attention] {name} full size: {rep}")
+    assert rep.steps == 8
