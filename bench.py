@@ -54,6 +54,9 @@ def parse_args():
     p.add_argument("--decode", choices=("fused", "split"), default="fused",
                    help="decode entry point: h2o_decode_step (fused) or h2o_decode_step_split")
     p.add_argument("--chunk-rows", type=int, default=0, help="split decode chunk length (0 = library's choice)")
+    p.add_argument("--prefill", choices=("select", "attention"), default="select",
+                   help="prefill entry point: h2o_prefill_select, or h2o_prefill_attention (also returns the "
+                        "prompt's attention output)")
     p.add_argument("--quant", choices=("none", "u8"), default="none",
                    help="cache storage: rows in the workload dtype, or 8-bit codes (h2o_cache_init_u8)")
     p.add_argument("--cpu-heads", type=int, default=256, help="heads in the CPU-oracle sample")
@@ -188,6 +191,8 @@ def main():
     caches = [H2OCache(B, H, d, wl.k_heavy, wl.k_recent, tdt, wl.scale, dev, quant="u8" if quant else None)
               for _ in range(L)]
     ws = caches[0].workspace(n)
+    attn = args.prefill == "attention"
+    prompt_out = torch.empty(B, H, n, d, dtype=torch.float32, device=dev) if attn else None
     outs = [torch.empty(B, H, d, dtype=torch.float32, device=dev) for _ in range(L)]
     evs = [torch.empty(B, H, dtype=torch.int32, device=dev) for _ in range(L)]
     qp = [qs[t].data_ptr() for t in range(T)]
@@ -214,8 +219,12 @@ def main():
                 check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
                                          ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
                                          c.score.data_ptr(), c.pos.data_ptr(), sh))
-            check(lib.h2o_prefill_select(ctypes.byref(c.desc), Q.data_ptr(), K.data_ptr(), V.data_ptr(), n,
-                                         ws.data_ptr(), ws.numel(), None, sh))
+            if attn:
+                check(lib.h2o_prefill_attention(ctypes.byref(c.desc), Q.data_ptr(), K.data_ptr(), V.data_ptr(), n,
+                                                ws.data_ptr(), ws.numel(), prompt_out.data_ptr(), None, None, sh))
+            else:
+                check(lib.h2o_prefill_select(ctypes.byref(c.desc), Q.data_ptr(), K.data_ptr(), V.data_ptr(), n,
+                                             ws.data_ptr(), ws.numel(), None, sh))
         if ev is not None:
             ev.record(stream)
         for t in range(T):
@@ -260,7 +269,8 @@ def main():
     mode = "u8" if quant else args.decode
     digest = decode_source_digest(mode)
     traffic = load_traffic(wl.name, digest, mode) if args.batch is None and args.heads is None else None
-    prefill_flops = 2.0 * n * (n + 1) * d * G  # two causal QK^T passes per layer
+    # two causal QK^T passes per layer (d n (n+1) flops each), plus the causal P.V with the output
+    prefill_flops = (3.0 if attn else 2.0) * n * (n + 1) * d * G
     pf_s = (sum(prefill_ms) / args.steps) / 1e3 / L
 
     single = None
@@ -306,7 +316,9 @@ def main():
         "decode_head_steps_per_s": head_steps / (sum(decode_ms) / args.steps / 1e3),
         "prefill": {"ms_per_layer": pf_s * 1e3, "algorithmic_TFLOPs": prefill_flops / pf_s / 1e12,
                     "mfma_frac": prefill_flops / pf_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                    "note": "rowlse + colsum + select/gather + cache clear, 2 causal QK^T passes"},
+                    "entry": args.prefill,
+                    "note": ("rowattn (QK^T + P.V, prompt output) + colsum (QK^T) + select/gather + cache clear"
+                             if attn else "rowlse + colsum + select/gather + cache clear, 2 causal QK^T passes")},
         "wall_s_timed": wall_s,
         "single_layer": single,
     }
