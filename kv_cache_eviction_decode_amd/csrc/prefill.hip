@@ -263,8 +263,14 @@ template <> __device__ __forceinline__ uint4 pack8<DT_F16>(const float* p) {
 // held by a lane are exactly the 8 k values the lane supplies as the B
 // operand of O^T = V^T P^T (k slot 8h+i <-> key 16g + 8(i/4) + 4h + i%4), so P
 // never leaves registers; V^T comes from the transposed LDS tile. The online
-// softmax keeps one running maximum per query column, shared by both lane
-// halves, and rescales the O accumulators when it grows.
+// softmax keeps one reference maximum per query column, shared by both lane
+// halves. It is raised only when a tile's maximum exceeds it by more than
+// kLazy (base-2 units, so probabilities stay below 2^kLazy), and the O
+// accumulators are rescaled only when some lane of the wave raised it: the
+// accumulators live in the accumulation registers, and a rescale on every
+// tile would cost more VALU work (moves and multiplies) than the MFMAs.
+// Numerator and denominator share the reference, so the result is exact.
+constexpr float kLazy = 8.0f;
 template <int DT, int D>
 __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
   using T = Tile64<DT, D>;
@@ -272,6 +278,7 @@ __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, i
   constexpr int NDB = D / 32;  // 32-channel blocks of the output
   __shared__ __attribute__((aligned(16))) char lds_k[2][T::BYTES];
   __shared__ __attribute__((aligned(16))) char lds_v[2][VT::BYTES];
+  __shared__ __attribute__((aligned(16))) char lds_q[4][T::BYTES];  // each wave's 64 query rows
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
   if (L >= G * nblk) return;  // uniform over the workgroup
   const int head = L / nblk;
@@ -286,14 +293,16 @@ __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, i
   const char* Vh = static_cast<const char*>(a.V) + size_t(head) * n * T::ROW;
   const float c = a.c;
 
-  uint4 qf[2][T::KS];
+  // The wave's query rows live in LDS (registers are needed for the O
+  // accumulators); they are read back as MFMA B fragments on every tile.
+  char* qbuf = lds_q[wave];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int r = min(q0 + cb * 32 + (lane & 31), n - 1);
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
+  for (int i = 0; i < 64 / T::RPI; ++i) {
+    const int row = i * T::RPI + lane / T::CH;
+    const int ch = lane % T::CH;
+    *reinterpret_cast<uint4*>(qbuf + row * T::RS + ch * 16) =
+        ld16(Qh + size_t(min(q0 + row, n - 1)) * T::ROW + ch * 16);
   }
-  wait_vmem_all();
   f32x16 o[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db][0] = o[db][1] = f32x16{};
@@ -324,7 +333,8 @@ __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, i
         for (int cb = 0; cb < 2; ++cb) {
           acc[kb][cb] = f32x16{};
 #pragma unroll
-          for (int ks = 0; ks < T::KS; ++ks) acc[kb][cb] = MfmaOp<DT>::run(af[ks], qf[cb][ks], acc[kb][cb]);
+          for (int ks = 0; ks < T::KS; ++ks)
+            acc[kb][cb] = MfmaOp<DT>::run(af[ks], T::frag(qbuf, cb, ks, lane), acc[kb][cb]);
         }
       }
       // acc[kb][cb][j] = s(query q0 + 32cb + lane%32, key key0 + 32kb + mfma_row(j))
@@ -344,9 +354,11 @@ __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, i
         for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][cb][j], acc[0][cb][j + 1]);
 #pragma unroll
         for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
-        const float mn = fmaxf(m[cb], fmaxf(tm, __shfl_xor(tm, 32)));  // same in both halves
+        const float tmax = fmaxf(tm, __shfl_xor(tm, 32));  // same in both halves
+        const bool raise = (tmax - m[cb]) * c > kLazy;         // also true while m = -inf
+        const float mn = raise ? tmax : m[cb];
         const float mnc = mn * c;
-        const float alpha = fast_exp2((m[cb] - mn) * c);
+        const float alpha = raise ? fast_exp2((m[cb] - mn) * c) : 1.0f;
         float t = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -361,8 +373,10 @@ __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, i
         }
         l[cb] = fmaf(l[cb], alpha, t);
         m[cb] = mn;
+        if (__ballot(raise)) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db][cb] *= alpha;
+          for (int db = 0; db < NDB; ++db) o[db][cb] *= alpha;
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
