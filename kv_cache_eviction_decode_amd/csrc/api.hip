@@ -8,6 +8,7 @@
 
 #include "../../include/h2o.h"
 #include "launch.h"
+#include "prefill_launch.h"
 
 namespace {
 

@@ -26,6 +26,7 @@
 
 #include "h2o_device.h"
 #include "launch.h"
+#include "prefill_launch.h"
 
 namespace h2o {
 namespace {
