@@ -67,23 +67,24 @@ __device__ __forceinline__ int mfma_row(int j, int lane) { return 8 * (j >> 2) +
 // tile is consumed, then writes it to the other LDS buffer (one barrier per
 // tile). Rows are padded by 16 bytes in LDS so that the 32 rows one MFMA
 // operand read touches fall into distinct banks.
-template <int DT, int D>
+template <int DT, int D, int NW = 4>
 struct Tile64 {
   static constexpr int E = Elem<DT>::bytes;
   static constexpr int ROW = D * E;       // bytes per row in global memory
   static constexpr int CH = ROW / 16;     // 16-byte chunks per row
   static constexpr int RS = ROW + 16;     // padded LDS row stride
   static constexpr int BYTES = 64 * RS;   // one 64-row tile
-  static constexpr int CPT = CH / 4;      // chunks per thread (256 threads, 64 rows)
+  static constexpr int CPT = CH / NW;     // chunks per thread (NW waves, 64 rows)
   static constexpr int RPI = 64 / CH;     // rows one wave-wide 16-byte access covers
   static constexpr int KS = D / 16;       // MFMA k-steps per row
+  static_assert(CPT >= 1, "tile too small for the workgroup");
 
-  // Thread (wave w, lane l) moves chunk l % CH of rows 16w + i*RPI + l / CH:
+  // Thread (wave w, lane l) moves chunk l % CH of rows (64/NW)w + i*RPI + l / CH:
   // each wave-wide access is 1 KiB of consecutive rows in global memory, and
   // consecutive lanes write consecutive 16-byte chunks of one LDS row (no
   // bank conflicts).
   __device__ __forceinline__ static int my_row(int i) {
-    return (threadIdx.x >> 6) * 16 + i * RPI + (threadIdx.x & 63) / CH;
+    return (threadIdx.x >> 6) * (64 / NW) + i * RPI + (threadIdx.x & 63) / CH;
   }
   __device__ __forceinline__ static int my_chunk() { return (threadIdx.x & 63) % CH; }
 
@@ -212,37 +213,6 @@ __global__ __launch_bounds__(256, 2) void rowlse_lds(PrefillArgs a, int nblk, in
 }
 
 // ---------------------------------------------------------------- pass 1 with output
-// The V tile of 64 keys is staged transposed in LDS for the P.V product:
-// channel row r holds the 64 keys' values of channel r. Within a row, groups
-// of 4 keys are permuted by XOR with the row's 8-channel chunk index, which
-// spreads the transposing 2-byte writes of one source row over distinct banks
-// while keeping every 4-key group contiguous for the 8-byte fragment reads.
-template <int DT, int D>
-struct VTileT {
-  using T = Tile64<DT, D>;
-  static constexpr int RS = 64 * 2 + 8;  // bytes per channel row (16-bit types), padded
-  static constexpr int BYTES = D * RS;
-  __device__ __forceinline__ static int phys(int key, int ch) { return key ^ ((ch & 15) << 2); }
-  __device__ __forceinline__ static void store(char* lds, const uint4 (&r)[T::CPT]) {
-#pragma unroll
-    for (int i = 0; i < T::CPT; ++i) {
-      const int key = T::my_row(i), ch = T::my_chunk();
-      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(lds + (ch * 8 + e) * RS + phys(key, ch) * 2) =
-            uint16_t(w[e >> 1] >> (16 * (e & 1)));
-    }
-  }
-  // A operand of the P.V MFMA: channel row d, keys key0 .. key0+3 and key0+8 .. key0+11.
-  __device__ __forceinline__ static uint4 frag(const char* lds, int d, int key0) {
-    const char* row = lds + d * RS;
-    const uint2 lo = *reinterpret_cast<const uint2*>(row + phys(key0, d >> 3) * 2);
-    const uint2 hi = *reinterpret_cast<const uint2*>(row + phys(key0 + 8, d >> 3) * 2);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-  }
-};
-
 // Eight probabilities as one 16-byte MFMA operand of the input type.
 template <int DT> __device__ __forceinline__ uint4 pack8(const float* p);
 template <> __device__ __forceinline__ uint4 pack8<DT_BF16>(const float* p) {
@@ -263,23 +233,58 @@ template <> __device__ __forceinline__ uint4 pack8<DT_F16>(const float* p) {
 // The S^T tiles are those of rowlse_lds; the probabilities of a 16-key group
 // held by a lane are exactly the 8 k values the lane supplies as the B
 // operand of O^T = V^T P^T (k slot 8h+i <-> key 16g + 8(i/4) + 4h + i%4), so P
-// never leaves registers; V^T comes from the transposed LDS tile. The online
+// never leaves registers; V^T comes from a transposed LDS tile. The online
 // softmax keeps one reference maximum per query column, shared by both lane
 // halves. It is raised only when a tile's maximum exceeds it by more than
 // kLazy (base-2 units, so probabilities stay below 2^kLazy), and the O
-// accumulators are rescaled only when some lane of the wave raised it: the
-// accumulators live in the accumulation registers, and a rescale on every
-// tile would cost more VALU work (moves and multiplies) than the MFMAs.
-// Numerator and denominator share the reference, so the result is exact.
+// accumulators are rescaled only when some lane of the wave raised it, which
+// after the first tiles is rare. Numerator and denominator share the
+// reference, so the result is exact.
 constexpr float kLazy = 8.0f;
+
+// Workgroup of 8 waves of 32 queries sharing the K and V tiles of 256
+// queries: a wave's O accumulators (d x 32), S tile and query fragments fit in
+// half the register file, so two waves run per SIMD and the softmax of one
+// overlaps the other's MFMAs (64 queries per wave at one wave per SIMD ran
+// 1.4x slower). The transposed V tile is laid out so that the 8 keys one lane
+// supplies to a P.V MFMA are adjacent (the two middle 4-key quads of every
+// 16-key group are swapped) and read with one 16-byte access; 8-key groups
+// are XOR-permuted per 8-channel chunk against bank conflicts.
 template <int DT, int D>
-__global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
-  using T = Tile64<DT, D>;
-  using VT = VTileT<DT, D>;
-  constexpr int NDB = D / 32;  // 32-channel blocks of the output
+struct VTile8 {
+  using T = Tile64<DT, D, 8>;
+  static constexpr int RS = 64 * 2 + 16;  // bytes per channel row (16-bit types), padded
+  static constexpr int BYTES = D * RS;
+  __device__ __forceinline__ static int phys(int key, int ch) {
+    const int q = (key >> 2) & 3;
+    const int qs = q == 1 ? 2 : q == 2 ? 1 : q;
+    return ((key & ~15) | (qs << 2) | (key & 3)) ^ ((ch & 7) << 3);
+  }
+  __device__ __forceinline__ static void store(char* lds, const uint4 (&r)[T::CPT]) {
+#pragma unroll
+    for (int i = 0; i < T::CPT; ++i) {
+      const int key = T::my_row(i), ch = T::my_chunk();
+      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = ch * 8 + e;
+        *reinterpret_cast<uint16_t*>(lds + d * RS + phys(key, d >> 3) * 2) = uint16_t(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+  // A operand of the P.V MFMA: channel row d, keys 16g + 4h + {0..3} and 16g + 8 + 4h + {0..3}.
+  __device__ __forceinline__ static uint4 frag(const char* lds, int d, int g, int h) {
+    return *reinterpret_cast<const uint4*>(lds + d * RS + phys(16 * g + 4 * h, d >> 3) * 2);
+  }
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
+  using T = Tile64<DT, D, 8>;
+  using VT = VTile8<DT, D>;
+  constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) char lds_k[2][T::BYTES];
   __shared__ __attribute__((aligned(16))) char lds_v[2][VT::BYTES];
-  __shared__ __attribute__((aligned(16))) char lds_q[4][T::BYTES];  // each wave's 64 query rows
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
   if (L >= G * nblk) return;  // uniform over the workgroup
   const int head = L / nblk;
@@ -288,26 +293,23 @@ __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, i
   const int lh = lane >> 5;
   const int n = a.n;
   const int wg_q0 = qb * 256;
-  const int q0 = wg_q0 + wave * 64;
+  const int q0 = wg_q0 + wave * 32;
   const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
   const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
   const char* Vh = static_cast<const char*>(a.V) + size_t(head) * n * T::ROW;
   const float c = a.c;
 
-  // The wave's query rows live in LDS (registers are needed for the O
-  // accumulators); they are read back as MFMA B fragments on every tile.
-  char* qbuf = lds_q[wave];
+  uint4 qf[T::KS];
+  {
+    const int r = min(q0 + (lane & 31), n - 1);
 #pragma unroll
-  for (int i = 0; i < 64 / T::RPI; ++i) {
-    const int row = i * T::RPI + lane / T::CH;
-    const int ch = lane % T::CH;
-    *reinterpret_cast<uint4*>(qbuf + row * T::RS + ch * 16) =
-        ld16(Qh + size_t(min(q0 + row, n - 1)) * T::ROW + ch * 16);
+    for (int ks = 0; ks < T::KS; ++ks) qf[ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
   }
-  f32x16 o[NDB][2];
+  wait_vmem_all();
+  f32x16 o[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db][0] = o[db][1] = f32x16{};
-  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  float m = kNegInf, l = 0.f;
   const int ntiles = min(wg_q0 + 255, n - 1) / 64 + 1;
   uint4 nk[T::CPT], nv[T::CPT];
   T::fetch(nk, Kh, 0, n);
@@ -315,6 +317,7 @@ __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, i
   T::store(lds_k[0], nk);
   VT::store(lds_v[0], nv);
   __syncthreads();
+  const int qi = q0 + (lane & 31);
   for (int kt = 0; kt < ntiles; ++kt) {
     if (kt + 1 < ntiles) {
       T::fetch(nk, Kh, (kt + 1) * 64, n);
@@ -323,72 +326,58 @@ __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, i
     const char* kbuf = lds_k[kt & 1];
     const char* vbuf = lds_v[kt & 1];
     const int key0 = kt * 64;
-    if (key0 <= min(q0 + 63, n - 1)) {  // every query of this wave sees key0
-      f32x16 acc[2][2];
+    if (key0 <= min(q0 + 31, n - 1)) {  // every query of this wave sees key0
+      f32x16 acc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        uint4 af[T::KS];
+        acc[kb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(kbuf, kb, ks, lane);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          acc[kb][cb] = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < T::KS; ++ks)
-            acc[kb][cb] = MfmaOp<DT>::run(af[ks], T::frag(qbuf, cb, ks, lane), acc[kb][cb]);
-        }
+        for (int ks = 0; ks < T::KS; ++ks) acc[kb] = MfmaOp<DT>::run(T::frag(kbuf, kb, ks, lane), qf[ks], acc[kb]);
       }
-      // acc[kb][cb][j] = s(query q0 + 32cb + lane%32, key key0 + 32kb + mfma_row(j))
-      uint4 pb[2][2][2];  // [cb][kb][g]: B operands of the P.V product
+      // acc[kb][j] = s(query qi, key key0 + 32kb + mfma_row(j))
+      if (key0 + 63 > q0) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int qi = q0 + cb * 32 + (lane & 31);
-        if (key0 + 63 > q0 + cb * 32) {  // tile reaches past some query of this block: mask
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int j = 0; j < 16; ++j)
+            if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][j] = kNegInf;
+      }
+      float tm = kNegInf;
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][cb][j] = kNegInf;
+      for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][j], acc[0][j + 1]);
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][j], acc[1][j + 1]);
+      const float tmax = fmaxf(tm, __shfl_xor(tm, 32));
+      const bool raise = (tmax - m) * c > kLazy;
+      const float mn = raise ? tmax : m;
+      const float mnc = mn * c;
+      const float alpha = raise ? fast_exp2((m - mn) * c) : 1.0f;
+      uint4 pb[2][2];
+      float t = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          p[j] = fast_exp2(fmaf(acc[kb][j], c, -mnc));
+          t += p[j];
         }
-        float tm = kNegInf;
+        pb[kb][0] = pack8<DT>(p);
+        pb[kb][1] = pack8<DT>(p + 8);
+      }
+      l = fmaf(l, alpha, t);
+      m = mn;
+      if (__ballot(raise)) {
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][cb][j], acc[0][cb][j + 1]);
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
-        const float tmax = fmaxf(tm, __shfl_xor(tm, 32));  // same in both halves
-        const bool raise = (tmax - m[cb]) * c > kLazy;         // also true while m = -inf
-        const float mn = raise ? tmax : m[cb];
-        const float mnc = mn * c;
-        const float alpha = raise ? fast_exp2((m[cb] - mn) * c) : 1.0f;
-        float t = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          float p[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            p[j] = fast_exp2(fmaf(acc[kb][cb][j], c, -mnc));
-            t += p[j];
-          }
-          pb[cb][kb][0] = pack8<DT>(p);
-          pb[cb][kb][1] = pack8<DT>(p + 8);
-        }
-        l[cb] = fmaf(l[cb], alpha, t);
-        m[cb] = mn;
-        if (__ballot(raise)) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) o[db][cb] *= alpha;
-        }
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const uint4 vf = VT::frag(vbuf, db * 32 + (lane & 31), kb * 32 + g * 16 + lh * 4);
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) o[db][cb] = MfmaOp<DT>::run(vf, pb[cb][kb][g], o[db][cb]);
-          }
+          for (int db = 0; db < NDB; ++db)
+            o[db] = MfmaOp<DT>::run(VT::frag(vbuf, db * 32 + (lane & 31), kb * 2 + g, lh), pb[kb][g], o[db]);
     }
     if (kt + 1 < ntiles) {
       T::store(lds_k[(kt + 1) & 1], nk);
@@ -396,27 +385,21 @@ __global__ __launch_bounds__(256, 1) void rowattn_lds(PrefillArgs a, int nblk, i
     }
     __syncthreads();
   }
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const float lt = l[cb] + __shfl_xor(l[cb], 32);  // both halves share the maximum
-    const int qi = q0 + cb * 32 + (lane & 31);
-    if (qi < n) {
-      const float lse2 = m[cb] * c + fast_log2(lt);
-      if (lh == 0) {
-        a.lse2[size_t(head) * ld_lse + qi] = lse2;
-        if (a.lse_out) a.lse_out[size_t(head) * n + qi] = lse2 * 0.6931471805599453f;
-      }
-      const float inv = 1.0f / lt;
-      float* orow = a.out + (size_t(head) * n + qi) * D;
-      // o[db][cb][j] = O(query qi, channel 32db + mfma_row(j))
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          *reinterpret_cast<float4*>(orow + db * 32 + 8 * jj + 4 * lh) =
-              make_float4(o[db][cb][4 * jj] * inv, o[db][cb][4 * jj + 1] * inv, o[db][cb][4 * jj + 2] * inv,
-                          o[db][cb][4 * jj + 3] * inv);
+  const float lt = l + __shfl_xor(l, 32);  // both halves share the reference maximum
+  if (qi < n) {
+    const float lse2 = m * c + fast_log2(lt);
+    if (lh == 0) {
+      a.lse2[size_t(head) * ld_lse + qi] = lse2;
+      if (a.lse_out) a.lse_out[size_t(head) * n + qi] = lse2 * 0.6931471805599453f;
     }
+    const float inv = 1.0f / lt;
+    float* orow = a.out + (size_t(head) * n + qi) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *reinterpret_cast<float4*>(orow + db * 32 + 8 * jj + 4 * lh) =
+            make_float4(o[db][4 * jj] * inv, o[db][4 * jj + 1] * inv, o[db][4 * jj + 2] * inv, o[db][4 * jj + 3] * inv);
   }
 }
 
@@ -885,7 +868,7 @@ hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
     if (a.pass1 == PASS1_LSE)
       hipLaunchKernelGGL((rowlse_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
     else if (a.pass1 == PASS1_ATTENTION)
-      hipLaunchKernelGGL((rowattn_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
+      hipLaunchKernelGGL((rowattn8_lds<DT, D>), dim3(grid), dim3(512), 0, s, a, nblk, G, ld_lse);
     hipLaunchKernelGGL((colsum_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
   }
   if (a.quant) {
