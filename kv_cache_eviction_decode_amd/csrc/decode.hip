@@ -514,12 +514,15 @@ hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
   constexpr int WMINW = 2;  // waves per SIMD the wave kernel is built for
   const int resident = cu_count() * 4 * WMINW;
   if (G >= resident / 2) {
-    constexpr int UB = 8, PF = 4;
+    // 4 wave-loads per batch (two batches in flight): 2% faster than 8 at the
+    // OPT-6.7B, OPT-30B and large-batch shapes.
+    constexpr int UB = 4, PF = 4;
     const int grid = G < resident ? G : resident;
     hipLaunchKernelGGL((decode_wave_kernel<DT, D, UB, PF, WMINW, SCORED>), dim3(grid), dim3(64), shmem, s, a, G);
   } else {
-    // Few heads: spread each head over a 4-wave workgroup instead.
-    constexpr int WAVES = 4, UB = 8, PF = 4, MINW = 1;
+    // Few heads: spread each head over a 4-wave workgroup instead (4-deep
+    // batches: 4% faster than 8 at 256 heads x 2048 slots).
+    constexpr int WAVES = 4, UB = 4, PF = 4, MINW = 1;
     hipLaunchKernelGGL((decode_kernel<DT, D, WAVES, UB, PF, MINW, SCORED>), dim3(G), dim3(WAVES * 64), shmem,
                        s, a);
   }

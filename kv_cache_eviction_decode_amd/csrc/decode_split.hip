@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 
 template <int DT, int D>
 hipError_t launch_split_typed(int G, const DecodeArgs& a, const SplitArgs& w, hipStream_t s) {
-  constexpr int UB = 8;
+  constexpr int UB = 4;  // 4-deep batches, as in the fused kernels
   const int64_t blocks = int64_t(G) * w.chunks;
   const size_t shmem = size_t(w.chunk_len) * sizeof(float);
   hipLaunchKernelGGL((decode_chunk_kernel<DT, D, UB>), dim3(uint32_t(blocks)), dim3(64), shmem, s, a, w);
