@@ -520,11 +520,15 @@ hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
     const int grid = G < resident ? G : resident;
     hipLaunchKernelGGL((decode_wave_kernel<DT, D, UB, PF, WMINW, SCORED>), dim3(grid), dim3(64), shmem, s, a, G);
   } else {
-    // Few heads: spread each head over a 4-wave workgroup instead (4-deep
-    // batches: 4% faster than 8 at 256 heads x 2048 slots).
-    constexpr int WAVES = 4, UB = 4, PF = 4, MINW = 1;
-    hipLaunchKernelGGL((decode_kernel<DT, D, WAVES, UB, PF, MINW, SCORED>), dim3(G), dim3(WAVES * 64), shmem,
-                       s, a);
+    // Few heads: spread each head over a 4-wave workgroup instead. With a
+    // workgroup per CU or more, 4-deep batches are 4% faster than 8 (256
+    // heads x 2048 slots); with fewer, each workgroup needs the deeper batches
+    // to keep enough bytes in flight (32 heads: 33 us against 39).
+    constexpr int WAVES = 4, PF = 4, MINW = 1;
+    if (G >= cu_count())
+      hipLaunchKernelGGL((decode_kernel<DT, D, WAVES, 4, PF, MINW, SCORED>), dim3(G), dim3(WAVES * 64), shmem, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<DT, D, WAVES, 8, PF, MINW, SCORED>), dim3(G), dim3(WAVES * 64), shmem, s, a);
   }
   return hipGetLastError();
 }
