@@ -107,6 +107,34 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
       }
       bias = group_sum<LPR>(part) * a.c;
     }
+    // The new token's codes do not depend on the step's attention, only the
+    // slot they go to does: quantise now, while the first rows are in flight
+    // (32 correctly rounded divisions per lane off the epilogue's path).
+    uint4 kn_codes, vn_codes;
+    float vs, vmn;
+    {
+      float kn[16], vn[16];
+      kn_raw.unpack(kn);
+      vn_raw.unpack(vn);
+      vmn = vn[0];
+      float vmx = vn[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        vmn = fminf(vmn, vn[i]);
+        vmx = fmaxf(vmx, vn[i]);
+      }
+      vmn = lane_group<LPR>(vmn, OpMin());
+      vmx = lane_group<LPR>(vmx, OpMax());
+      vs = u8_grid_scale(vmn, vmx);
+      uint32_t kc[16], vc[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        kc[i] = quantize_u8(kn[i], ks[i], km[i]);
+        vc[i] = quantize_u8(vn[i], vs, vmn);
+      }
+      kn_codes = pack_codes(kc);
+      vn_codes = pack_codes(vc);
+    }
     float sc_pf[PF];
     int pos_pf[PF];
 #pragma unroll
@@ -285,24 +313,9 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
         sc_g[victim] = p_new;
         pos_g[victim] = a.t;
       }
-      float vmn = vn[0], vmx = vn[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) {
-        vmn = fminf(vmn, vn[i]);
-        vmx = fmaxf(vmx, vn[i]);
-      }
-      vmn = lane_group<LPR>(vmn, OpMin());
-      vmx = lane_group<LPR>(vmx, OpMax());
-      const float vs = u8_grid_scale(vmn, vmx);
       if (grp == 0) {
-        uint32_t kc[16], vc[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          kc[i] = quantize_u8(kn[i], ks[i], km[i]);
-          vc[i] = quantize_u8(vn[i], vs, vmn);
-        }
-        st16(static_cast<uint8_t*>(a.K_w) + (hrow + victim) * D + c0, pack_codes(kc));
-        st16(static_cast<uint8_t*>(a.V_w) + (hrow + victim) * D + c0, pack_codes(vc));
+        st16(static_cast<uint8_t*>(a.K_w) + (hrow + victim) * D + c0, kn_codes);
+        st16(static_cast<uint8_t*>(a.V_w) + (hrow + victim) * D + c0, vn_codes);
         if (sub == 0) reinterpret_cast<float2*>(a.v_qparam)[hrow + victim] = make_float2(vs, vmn);
       }
     }
