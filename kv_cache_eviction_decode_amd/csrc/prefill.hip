@@ -246,35 +246,37 @@ constexpr float kLazy = 8.0f;
 // queries: a wave's O accumulators (d x 32), S tile and query fragments fit in
 // half the register file, so two waves run per SIMD and the softmax of one
 // overlaps the other's MFMAs (64 queries per wave at one wave per SIMD ran
-// 1.4x slower). The transposed V tile is laid out so that the 8 keys one lane
-// supplies to a P.V MFMA are adjacent (the two middle 4-key quads of every
-// 16-key group are swapped) and read with one 16-byte access; 8-key groups
-// are XOR-permuted per 8-channel chunk against bank conflicts.
+// 1.4x slower). V is staged in LDS as it is in memory (key rows) and its
+// MFMA A operands (channel rows) are read with gfx950's transposing LDS
+// read; a V tile transposed while staging took 2-byte LDS writes that
+// collided on banks.
 template <int DT, int D>
 struct VTile8 {
   using T = Tile64<DT, D, 8>;
-  static constexpr int RS = 64 * 2 + 16;  // bytes per channel row (16-bit types), padded
-  static constexpr int BYTES = D * RS;
-  __device__ __forceinline__ static int phys(int key, int ch) {
-    const int q = (key >> 2) & 3;
-    const int qs = q == 1 ? 2 : q == 2 ? 1 : q;
-    return ((key & ~15) | (qs << 2) | (key & 3)) ^ ((ch & 7) << 3);
-  }
+  static constexpr int RS = T::ROW + 32;  // bytes per key row: 4 consecutive rows fall 8 banks apart
+  static constexpr int BYTES = 64 * RS;
   __device__ __forceinline__ static void store(char* lds, const uint4 (&r)[T::CPT]) {
 #pragma unroll
-    for (int i = 0; i < T::CPT; ++i) {
-      const int key = T::my_row(i), ch = T::my_chunk();
-      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = ch * 8 + e;
-        *reinterpret_cast<uint16_t*>(lds + d * RS + phys(key, d >> 3) * 2) = uint16_t(w[e >> 1] >> (16 * (e & 1)));
-      }
-    }
+    for (int i = 0; i < T::CPT; ++i)
+      *reinterpret_cast<uint4*>(lds + T::my_row(i) * RS + T::my_chunk() * 16) = r[i];
   }
-  // A operand of the P.V MFMA: channel row d, keys 16g + 4h + {0..3} and 16g + 8 + 4h + {0..3}.
-  __device__ __forceinline__ static uint4 frag(const char* lds, int d, int g, int h) {
-    return *reinterpret_cast<const uint4*>(lds + d * RS + phys(16 * g + 4 * h, d >> 3) * 2);
+  // A operand of the P.V MFMA for 32-channel block db and 16-key group g:
+  // channel 32db + lane%32, keys 16g + 4h + {0..3} then 16g + 8 + 4h + {0..3}
+  // (h = lane/32). The transposing LDS read gives lane i of each 16-lane group
+  // element i%4 of the 8-byte rows read by lanes i/4, i/4 + 4, i/4 + 8 and
+  // i/4 + 12 of the group, so lane s reads key row 16g + 4h + s/4 (+8) at
+  // channel 32db + 16 * (group % 2) + 4 * (s % 4).
+  __device__ __forceinline__ static uint4 frag(const char* lds, int db, int g, int lane) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const int s = lane & 15;
+    const int row = 16 * g + 4 * (lane >> 5) + (s >> 2);
+    const int ch = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const char* p = lds + row * RS + ch * 2;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 8 * RS));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return make_uint4(l2.x, l2.y, h2.x, h2.y);
   }
 };
 
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
-            o[db] = MfmaOp<DT>::run(VT::frag(vbuf, db * 32 + (lane & 31), kb * 2 + g, lh), pb[kb][g], o[db]);
+            o[db] = MfmaOp<DT>::run(VT::frag(vbuf, db, kb * 2 + g, lane), pb[kb][g], o[db]);
     }
     if (kt + 1 < ntiles) {
       T::store(lds_k[(kt + 1) & 1], nk);
