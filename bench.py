@@ -142,7 +142,7 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
               "the H2O path shards by (batch, head) with no communication, so a multi-GPU run "
-              "is the same kernel on each GPU's share and is not part of this build.", file=sys.stderr)
+              "is the same kernel on each GPU's share; this benchmark measures one GPU only.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -81,7 +81,7 @@ typedef enum { H2O_POLICY_ACCUMULATED = 0, H2O_POLICY_AVERAGED = 1, H2O_POLICY_P
  */
 typedef enum { H2O_QUANT_NONE = 0, H2O_QUANT_U8 = 1 } h2o_quant;
 
-/* Limits of this build. */
+/* Size limits that the library checks (H2O_EINVAL beyond them). */
 #define H2O_MAX_SLOTS 8192      /* k = k_heavy + k_recent */
 #define H2O_MAX_PROMPT 1048576  /* n */
 
