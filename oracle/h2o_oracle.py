@@ -52,10 +52,10 @@ Policies (the variants the page compares H2O with or reports as worse):
   heavy-hitter-only ablation (H2O §5 "Ablation and Extended Evaluations");
   with k_recent = 0 the new token itself competes and may be the one evicted.
 
-Quantised cache (quant="u8", oracle/quant.py): cached keys and values are
-held as 8-bit codes, keys on per-channel grids fixed by the prompt, values on
-per-token grids (the KIVI finding in Discoveries (cursor 150); H2O combined
-with quantisation, H2O §5). Attention reads the dequantised rows; the new
+Quantised cache (quant="u8", "u4" or "u2", oracle/quant.py): cached keys and
+values are held as 8-, 4- or 2-bit codes, keys on per-channel grids fixed by
+the prompt, values on per-token grids (the KIVI finding in Discoveries (cursor
+150); H2O combined with quantisation, H2O §5). Attention reads the dequantised rows; the new
 token attends to its own key and value at full precision and is quantised
 when it is written into its slot. Scores, selection and eviction are as
 above. An empty prompt leaves nothing to calibrate the key grids on, so a
@@ -232,10 +232,11 @@ class H2OOracle:
             raise ValueError("need k_heavy >= 0, k_recent >= 0 and k >= 1")
         if policy not in POLICIES:
             raise ValueError(f"unknown policy {policy!r}")
-        if quant not in (None, "u8"):
+        if quant is not None and quant not in qz.BITS:
             raise ValueError(f"unknown quantisation {quant!r}")
         self.policy = policy
         self.quant = quant
+        self.bits = qz.BITS[quant] if quant else None
         self.G, self.d = n_heads, head_dim
         self.k_heavy, self.k_recent = k_heavy, k_recent
         self.k = k_heavy + k_recent
@@ -263,9 +264,9 @@ class H2OOracle:
             return
         k_rows32 = np.asarray(k_rows, np.float32)  # float32-exact inputs
         v_rows32 = np.asarray(v_rows, np.float32)
-        kc = qz.quantize(k_rows32, self.k_scale[g], self.k_min[g])
-        vs, vm = qz.row_grid(v_rows32)
-        vc = qz.quantize(v_rows32, vs[..., None], vm[..., None])
+        kc = qz.quantize(k_rows32, self.k_scale[g], self.k_min[g], self.bits)
+        vs, vm = qz.row_grid(v_rows32, self.bits)
+        vc = qz.quantize(v_rows32, vs[..., None], vm[..., None], self.bits)
         self.Kq[g, slots], self.Vq[g, slots] = kc, vc
         self.v_scale[g, slots], self.v_min[g, slots] = vs, vm
         self.K[g, slots] = qz.dequantize(kc, self.k_scale[g], self.k_min[g])
@@ -292,7 +293,7 @@ class H2OOracle:
             self.pos[g, :m] = keep
             self.score[g, :m] = colsum[g][keep]
             if self.quant:
-                self.k_scale[g], self.k_min[g] = qz.channel_grid(K[g])
+                self.k_scale[g], self.k_min[g] = qz.channel_grid(K[g], self.bits)
             self._store_rows(g, np.arange(m), K[g][keep], V[g][keep])
         self.n_used = min(n, self.k)
         self.t = n
