@@ -33,7 +33,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
 METRIC = "H2O decode head-steps/sec + achieved HBM GB/s (% of MI355X peak)"
 DECODE_SOURCES = {"fused": ["decode.hip", "h2o_device.h", "launch.h"],
                   "split": ["decode_split.hip", "h2o_device.h", "launch.h"],
-                  "u8": ["decode_u8.hip", "h2o_device.h", "launch.h"]}
+                  "u8": ["decode_quant.hip", "h2o_device.h", "launch.h"],
+                  "u4": ["decode_quant.hip", "h2o_device.h", "launch.h"],
+                  "u2": ["decode_quant.hip", "h2o_device.h", "launch.h"]}
+QUANT_BITS = {"u8": 8, "u4": 4, "u2": 2}
 
 
 def log(*a):
@@ -57,8 +60,9 @@ def parse_args():
     p.add_argument("--prefill", choices=("select", "attention"), default="select",
                    help="prefill entry point: h2o_prefill_select, or h2o_prefill_attention (also returns the "
                         "prompt's attention output)")
-    p.add_argument("--quant", choices=("none", "u8"), default="none",
-                   help="cache storage: rows in the workload dtype, or 8-bit codes (h2o_cache_init_u8)")
+    p.add_argument("--quant", choices=("none", "u8", "u4", "u2"), default="none",
+                   help="cache storage: rows in the workload dtype, or 8-, 4- or 2-bit codes "
+                        "(h2o_cache_init_quant)")
     p.add_argument("--cpu-heads", type=int, default=256, help="heads in the CPU-oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-single-layer", action="store_true")
@@ -85,11 +89,12 @@ def decode_bytes_per_head(n_used: int, d: int, e: int) -> int:
     return 2 * n_used * d * e + 12 * n_used + 5 * d * e + 4 * d + 8
 
 
-def decode_bytes_per_head_u8(n_used: int, d: int, e: int) -> int:
-    """The same for an 8-bit cache: codes instead of rows, plus the value grid
-    of every occupied slot and the head's key grids; the new token's codes and
-    value grid are written."""
-    return 2 * n_used * d + 8 * n_used + 12 * n_used + 3 * d * e + 8 * d + 4 * d + 2 * d + 8 + 8
+def decode_bytes_per_head_quant(n_used: int, d: int, e: int, bits: int) -> int:
+    """The same for a cache of bits-wide codes: packed codes instead of rows
+    (d * bits / 8 bytes each), plus the value grid of every occupied slot and
+    the head's key grids; the new token's codes and value grid are written."""
+    rb = d * bits // 8
+    return 2 * n_used * rb + 8 * n_used + 12 * n_used + 3 * d * e + 8 * d + 4 * d + 2 * rb + 8 + 8
 
 
 def load_traffic(workload: str, digest: str, mode: str = "fused"):
@@ -185,11 +190,12 @@ def main():
 
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
-    quant = args.quant == "u8"
+    quant = args.quant != "none"
     if quant and args.decode == "split":
         raise SystemExit("the split decode entry point takes caches stored in their dtype only")
-    caches = [H2OCache(B, H, d, wl.k_heavy, wl.k_recent, tdt, wl.scale, dev, quant="u8" if quant else None)
+    caches = [H2OCache(B, H, d, wl.k_heavy, wl.k_recent, tdt, wl.scale, dev, quant=args.quant if quant else None)
               for _ in range(L)]
+    qcode = {"u8": 1, "u4": 2, "u2": 3}.get(args.quant, 0)
     ws = caches[0].workspace(n)
     attn = args.prefill == "attention"
     prompt_out = torch.empty(B, H, n, d, dtype=torch.float32, device=dev) if attn else None
@@ -211,10 +217,10 @@ def main():
         for i in layers:
             c = caches[i]
             if quant:
-                check(lib.h2o_cache_init_u8(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
-                                            ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
-                                            c.k_qparam.data_ptr(), c.v_qparam.data_ptr(),
-                                            c.score.data_ptr(), c.pos.data_ptr(), sh))
+                check(lib.h2o_cache_init_quant(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
+                                               ctypes.c_float(wl.scale), qcode, c.K.data_ptr(), c.V.data_ptr(),
+                                               c.k_qparam.data_ptr(), c.v_qparam.data_ptr(),
+                                               c.score.data_ptr(), c.pos.data_ptr(), sh))
             else:
                 check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
                                          ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
@@ -261,12 +267,15 @@ def main():
     value = head_steps / (ms_per_step / 1e3)
 
     n_used = [min(k, n + t) for t in range(T)]
-    per_head = decode_bytes_per_head_u8 if quant else decode_bytes_per_head
-    bytes_per_launch = G * sum(per_head(u, d, e) for u in n_used) / T
+    if quant:
+        bits = QUANT_BITS[args.quant]
+        bytes_per_launch = G * sum(decode_bytes_per_head_quant(u, d, e, bits) for u in n_used) / T
+    else:
+        bytes_per_launch = G * sum(decode_bytes_per_head(u, d, e) for u in n_used) / T
     launches = T * L
     avg_launch_s = (sum(decode_ms) / args.steps) / 1e3 / launches
     achieved = bytes_per_launch / avg_launch_s / 1e9
-    mode = "u8" if quant else args.decode
+    mode = args.quant if quant else args.decode
     digest = decode_source_digest(mode)
     traffic = load_traffic(wl.name, digest, mode) if args.batch is None and args.heads is None else None
     # two causal QK^T passes per layer (d n (n+1) flops each), plus the causal P.V with the output
@@ -305,11 +314,11 @@ def main():
         "config": {"workload": wl.name, "batch": B, "heads": H, "head_dim": d, "prompt_len": n,
                    "k_heavy": wl.k_heavy, "k_recent": wl.k_recent, "decode_steps": T, "layers": L,
                    "pareto_alpha": wl.alpha, "parallelism": "none (1 GPU)", "decode_entry": args.decode,
-                   "cache_storage": "u8 codes" if quant else wl.dtype},
+                   "cache_storage": f"{args.quant} codes" if quant else wl.dtype},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ("h2o decode_chunk_kernel + decode_merge_kernel (split decode)" if split else
-                                "h2o decode_u8_kernel (fused step over 8-bit codes)" if quant else
+                                f"h2o decode_quant_kernel (fused step over {args.quant} codes)" if quant else
                                 "h2o decode_kernel (fused attention + score + evict + insert)"),
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
                      "kernel_source_digest": digest},

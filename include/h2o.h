@@ -66,20 +66,24 @@ typedef enum { H2O_POLICY_ACCUMULATED = 0, H2O_POLICY_AVERAGED = 1, H2O_POLICY_P
 
 /*
  * Storage of a cache's keys and values:
- *   NONE - rows in the cache dtype, as handed in;
- *   U8   - 8-bit codes (H2O combined with quantisation, H2O §5 "Ablation and
- *          Extended Evaluations"; keys per channel and values per token, after
- *          the KIVI abstract on the page "Discoveries (cursor 150)"). Keys use
- *          one affine grid per (batch, head, channel), fixed by the prompt:
- *          mn_c and mx_c are the prompt's smallest and largest key values in
- *          channel c and scale_c = (mx_c - mn_c) / 255. Values use one grid per
+ *   NONE       - rows in the cache dtype, as handed in;
+ *   U8, U4, U2 - b = 8, 4 or 2-bit codes (H2O combined with quantisation,
+ *          H2O §5 "Ablation and Extended Evaluations"; keys per channel and
+ *          values per token, down to 2 bits, after the KIVI abstract on the
+ *          page "Discoveries (cursor 150)"). With L = 2^b - 1: keys use one
+ *          affine grid per (batch, head, channel), fixed by the prompt: mn_c
+ *          and mx_c are the prompt's smallest and largest key values in
+ *          channel c and scale_c = (mx_c - mn_c) / L. Values use one grid per
  *          cached row over its own d values. A value x is stored as the code
- *          rint((x - mn) / scale) clamped to [0, 255] (0 if scale = 0), all in
+ *          rint((x - mn) / scale) clamped to [0, L] (0 if scale = 0), all in
  *          fp32 with IEEE rounding and ties to even, and read as
- *          code * scale + mn. A decode token attends to its own key and value
- *          at full precision; it is quantised when written into its slot.
+ *          code * scale + mn. A row of head_dim codes takes head_dim * b / 8
+ *          bytes; channel c sits in byte c * b / 8 at bit offset
+ *          b * (c mod 8/b), low bits first. A decode token attends to its own
+ *          key and value at full precision; it is quantised when written into
+ *          its slot.
  */
-typedef enum { H2O_QUANT_NONE = 0, H2O_QUANT_U8 = 1 } h2o_quant;
+typedef enum { H2O_QUANT_NONE = 0, H2O_QUANT_U8 = 1, H2O_QUANT_U4 = 2, H2O_QUANT_U2 = 3 } h2o_quant;
 
 /* Size limits that the library checks (H2O_EINVAL beyond them). */
 #define H2O_MAX_SLOTS 8192      /* k = k_heavy + k_recent */
@@ -140,16 +144,27 @@ h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_
                           h2o_stream_t stream);
 
 /*
- * As h2o_cache_init, for a cache stored as 8-bit codes (H2O_QUANT_U8, see
- * h2o_quant). dtype is that of the queries, keys and values handed to prefill
- * and decode; the cache holds
- *   Kq, Vq   : [batch][heads][k][head_dim] uint8 codes, slot-indexed rows
- *   k_qparam : [batch][heads][2][head_dim] fp32, written by prefill
- *   v_qparam : [batch][heads][k][2] fp32
+ * As h2o_cache_init, for a cache stored as codes (quant = H2O_QUANT_U8,
+ * H2O_QUANT_U4 or H2O_QUANT_U2, b = 8, 4 or 2 bits, see h2o_quant). dtype is
+ * that of the queries, keys and values handed to prefill and decode; the
+ * cache holds
+ *   Kq, Vq   : [batch][heads][k][head_dim * b / 8] uint8 packed codes,
+ *              slot-indexed rows
+ *   k_qparam : [batch][heads][2][head_dim] fp32 (scales, then minima),
+ *              written by prefill
+ *   v_qparam : [batch][heads][k][2] fp32 (scale, minimum of each row)
  * with score and pos as for h2o_cache_init. Kq, Vq, k_qparam and v_qparam
  * must be 16-byte aligned. The prompt handed to prefill must have n >= 1
  * (it fixes the key grids). h2o_decode_step_split does not take such a cache.
+ * Errors: H2O_EINVAL for an unknown quant value or a missing buffer, plus
+ * those of h2o_cache_init.
  */
+h2o_status h2o_cache_init_quant(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                                int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype,
+                                float scale, int32_t quant, uint8_t* Kq, uint8_t* Vq, float* k_qparam,
+                                float* v_qparam, float* score, int32_t* pos, h2o_stream_t stream);
+
+/* h2o_cache_init_quant with quant = H2O_QUANT_U8. */
 h2o_status h2o_cache_init_u8(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
                              int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype,
                              float scale, uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam,

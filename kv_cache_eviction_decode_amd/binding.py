@@ -25,7 +25,9 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "h2o.h")
 H2O_OK, H2O_EINVAL, H2O_ESTATE, H2O_EWORKSPACE, H2O_EDEVICE = 0, 1, 2, 3, 4
 H2O_F32, H2O_BF16, H2O_F16 = 0, 1, 2
 H2O_POLICY_ACCUMULATED, H2O_POLICY_AVERAGED, H2O_POLICY_POSITION = 0, 1, 2
-H2O_QUANT_NONE, H2O_QUANT_U8 = 0, 1
+H2O_QUANT_NONE, H2O_QUANT_U8, H2O_QUANT_U4, H2O_QUANT_U2 = 0, 1, 2, 3
+QUANT_CODE = {"u8": H2O_QUANT_U8, "u4": H2O_QUANT_U4, "u2": H2O_QUANT_U2}
+QUANT_BITS = {"u8": 8, "u4": 4, "u2": 2}
 POLICY_CODE = {"accumulated": H2O_POLICY_ACCUMULATED, "averaged": H2O_POLICY_AVERAGED,
                "position": H2O_POLICY_POSITION}
 DTYPE_CODE = {torch.float32: H2O_F32, torch.bfloat16: H2O_BF16, torch.float16: H2O_F16}
@@ -78,6 +80,8 @@ _SIGNATURES = {
                             _P, _P, _P, _P, _P]),
     "h2o_cache_init_u8": (_I, [ctypes.POINTER(h2o_cache), _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                                _P, _P, _P, _P, _P, _P, _P]),
+    "h2o_cache_init_quant": (_I, [ctypes.POINTER(h2o_cache), _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
+                                  _P, _P, _P, _P, _P, _P, _P]),
     "h2o_prefill_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "h2o_prefill_select": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _I, _P, ctypes.c_size_t, _P, _P]),
     "h2o_prefill_attention": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _I, _P, ctypes.c_size_t, _P, _P, _P,
@@ -169,24 +173,35 @@ def h2o_cache_init(desc: h2o_cache, batch, heads, head_dim, k_heavy, k_recent, p
                                          _ptr(score), _ptr(pos), _stream_handle(stream)))
 
 
-def h2o_cache_init_u8(desc: h2o_cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale,
-                      Kq: torch.Tensor, Vq: torch.Tensor, k_qparam: torch.Tensor, v_qparam: torch.Tensor,
-                      score: torch.Tensor, pos: torch.Tensor, stream=None):
+def h2o_cache_init_quant(desc: h2o_cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale,
+                         quant: str, Kq: torch.Tensor, Vq: torch.Tensor, k_qparam: torch.Tensor,
+                         v_qparam: torch.Tensor, score: torch.Tensor, pos: torch.Tensor, stream=None):
+    """quant: "u8", "u4" or "u2"; Kq and Vq hold head_dim * bits / 8 bytes per row."""
     k = k_heavy + k_recent
     if dtype not in DTYPE_CODE:
         raise ValueError(f"unsupported dtype {dtype}")
+    if quant not in QUANT_CODE:
+        raise ValueError(f"unknown quantisation {quant!r}")
     dev = Kq.device
-    _expect(Kq, "Kq", (batch, heads, k, head_dim), torch.uint8)
-    _expect(Vq, "Vq", (batch, heads, k, head_dim), torch.uint8, dev)
+    rb = head_dim * QUANT_BITS[quant] // 8
+    _expect(Kq, "Kq", (batch, heads, k, rb), torch.uint8)
+    _expect(Vq, "Vq", (batch, heads, k, rb), torch.uint8, dev)
     _expect(k_qparam, "k_qparam", (batch, heads, 2, head_dim), torch.float32, dev)
     _expect(v_qparam, "v_qparam", (batch, heads, k, 2), torch.float32, dev)
     _expect(score, "score", (batch, heads, k), torch.float32, dev)
     _expect(pos, "pos", (batch, heads, k), torch.int32, dev)
     code = POLICY_CODE.get(policy, policy) if isinstance(policy, str) else int(policy)
-    _check(load_library().h2o_cache_init_u8(ctypes.byref(desc), batch, heads, head_dim, k_heavy, k_recent,
-                                            code, DTYPE_CODE[dtype], float(scale), _ptr(Kq), _ptr(Vq),
-                                            _ptr(k_qparam), _ptr(v_qparam), _ptr(score), _ptr(pos),
-                                            _stream_handle(stream)))
+    _check(load_library().h2o_cache_init_quant(ctypes.byref(desc), batch, heads, head_dim, k_heavy, k_recent,
+                                               code, DTYPE_CODE[dtype], float(scale), QUANT_CODE[quant],
+                                               _ptr(Kq), _ptr(Vq), _ptr(k_qparam), _ptr(v_qparam), _ptr(score),
+                                               _ptr(pos), _stream_handle(stream)))
+
+
+def h2o_cache_init_u8(desc: h2o_cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale,
+                      Kq, Vq, k_qparam, v_qparam, score, pos, stream=None):
+    """h2o_cache_init_quant with 8-bit codes."""
+    h2o_cache_init_quant(desc, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, "u8",
+                         Kq, Vq, k_qparam, v_qparam, score, pos, stream)
 
 
 def _desc_dtype(desc):
@@ -307,9 +322,10 @@ def h2o_fullcache_decode(q, Kc, Vc, out, scale, stream=None):
 class H2OCache:
     """One layer's H2O cache: torch-allocated device tensors plus the C descriptor.
 
-    quant=None stores rows in `dtype`; quant="u8" stores 8-bit codes (K and V
-    are then uint8, with the grids in k_qparam and v_qparam) and `dtype` is
-    that of the queries, keys and values handed in.
+    quant=None stores rows in `dtype`; quant="u8", "u4" or "u2" stores 8-, 4- or
+    2-bit codes (K and V are then uint8 [batch, heads, k, head_dim * bits / 8],
+    with the grids in k_qparam and v_qparam) and `dtype` is that of the
+    queries, keys and values handed in.
     """
 
     def __init__(self, batch, heads, head_dim, k_heavy, k_recent, dtype=torch.bfloat16,
@@ -318,12 +334,13 @@ class H2OCache:
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
-        if quant not in (None, "u8"):
+        if quant is not None and quant not in QUANT_CODE:
             raise ValueError(f"unknown quantisation {quant!r}")
         self.quant = quant
         self.dtype = dtype
         store = torch.uint8 if quant else dtype
-        self.K = torch.zeros(batch, heads, k, head_dim, dtype=store, device=self.device)
+        row = head_dim * QUANT_BITS[quant] // 8 if quant else head_dim
+        self.K = torch.zeros(batch, heads, k, row, dtype=store, device=self.device)
         self.V = torch.zeros_like(self.K)
         self.score = torch.zeros(batch, heads, k, dtype=torch.float32, device=self.device)
         self.pos = torch.full((batch, heads, k), -1, dtype=torch.int32, device=self.device)
@@ -334,8 +351,8 @@ class H2OCache:
         if quant:
             self.k_qparam = torch.zeros(batch, heads, 2, head_dim, dtype=torch.float32, device=self.device)
             self.v_qparam = torch.zeros(batch, heads, k, 2, dtype=torch.float32, device=self.device)
-            h2o_cache_init_u8(self.desc, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, self.scale,
-                              self.K, self.V, self.k_qparam, self.v_qparam, self.score, self.pos, stream)
+            h2o_cache_init_quant(self.desc, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, self.scale,
+                                 quant, self.K, self.V, self.k_qparam, self.v_qparam, self.score, self.pos, stream)
         else:
             h2o_cache_init(self.desc, batch, heads, head_dim, k_heavy, k_recent, policy, self.scale,
                            self.K, self.V, self.score, self.pos, stream)

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libh2o.so")
-SOURCES = ["api.hip", "decode.hip", "decode_split.hip", "decode_u8.hip", "prefill.hip"]
+SOURCES = ["api.hip", "decode.hip", "decode_split.hip", "decode_quant.hip", "prefill.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops (v_pk_*_f32) are disabled for all device code.

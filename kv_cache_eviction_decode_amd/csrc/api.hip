@@ -32,6 +32,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int elem_bytes(int32_t dtype) { return dtype == H2O_F32 ? 4 : 2; }
 
+// Bits per code of a quantised cache.
+int code_bits(int32_t quant) { return quant == H2O_QUANT_U8 ? 8 : quant == H2O_QUANT_U4 ? 4 : 2; }
+
 h2o_status check_cache(const h2o_cache* c) {
   if (!c) return fail(H2O_EINVAL, "cache is NULL");
   if (c->magic != kMagic) return fail(H2O_ESTATE, "cache descriptor was not initialised by h2o_cache_init");
@@ -103,7 +106,7 @@ h2o_status prefill(h2o_cache* cache, const void* Q, const void* Kp, const void* 
   if (cache->t_next != 0) return fail(H2O_ESTATE, "prefill needs a freshly initialised cache (t_next = %d)", cache->t_next);
   if (n < 0 || n > H2O_MAX_PROMPT) return fail(H2O_EINVAL, "prompt length %d out of range [0, %d]", n, H2O_MAX_PROMPT);
   if (n == 0 && cache->quant != H2O_QUANT_NONE)
-    return fail(H2O_EINVAL, "an 8-bit cache needs a prompt of at least one token (it fixes the key grids)");
+    return fail(H2O_EINVAL, "a cache stored as codes needs a prompt of at least one token (it fixes the key grids)");
   if (n == 0) return H2O_OK;  // nothing to score; the cleared cache is the result
   if (!Q || !Kp || !Vp) return fail(H2O_EINVAL, "Q, K and V must be non-NULL");
   if (!aligned(Q, 16) || !aligned(Kp, 16) || !aligned(Vp, 16))
@@ -161,15 +164,25 @@ h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_
                     H2O_QUANT_NONE, nullptr, nullptr, stream);
 }
 
-h2o_status h2o_cache_init_u8(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
-                             int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
-                             uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam, float* score,
-                             int32_t* pos, h2o_stream_t stream) {
+h2o_status h2o_cache_init_quant(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                                int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
+                                int32_t quant, uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam,
+                                float* score, int32_t* pos, h2o_stream_t stream) {
+  if (quant != H2O_QUANT_U8 && quant != H2O_QUANT_U4 && quant != H2O_QUANT_U2)
+    return fail(H2O_EINVAL, "unknown code format %d (H2O_QUANT_U8, _U4 or _U2)", quant);
   if (!k_qparam || !v_qparam) return fail(H2O_EINVAL, "k_qparam and v_qparam must be non-NULL");
   if (!aligned(k_qparam, 16) || !aligned(v_qparam, 16))
     return fail(H2O_EINVAL, "k_qparam and v_qparam must be 16-byte aligned");
   return init_cache(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, Kq, Vq, score, pos,
-                    H2O_QUANT_U8, k_qparam, v_qparam, stream);
+                    quant, k_qparam, v_qparam, stream);
+}
+
+h2o_status h2o_cache_init_u8(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
+                             int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
+                             uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam, float* score,
+                             int32_t* pos, h2o_stream_t stream) {
+  return h2o_cache_init_quant(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, H2O_QUANT_U8,
+                              Kq, Vq, k_qparam, v_qparam, score, pos, stream);
 }
 
 size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n) {
@@ -237,8 +250,9 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, c
   a.v_qparam = cache->v_qparam;
   const int G = cache->batch * cache->heads;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = device_status(cache->quant == H2O_QUANT_U8 ? h2o::launch_decode_u8(cache->dtype, cache->head_dim, G, a, s)
-                                                  : h2o::launch_decode(cache->dtype, cache->head_dim, G, a, s),
+  st = device_status(cache->quant != H2O_QUANT_NONE
+                         ? h2o::launch_decode_quant(code_bits(cache->quant), cache->dtype, cache->head_dim, G, a, s)
+                         : h2o::launch_decode(cache->dtype, cache->head_dim, G, a, s),
                      "h2o_decode_step");
   if (st != H2O_OK) return st;
   cache->t_next += 1;

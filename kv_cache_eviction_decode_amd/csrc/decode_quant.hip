@@ -1,4 +1,4 @@
-// H2O decode step over a cache stored as 8-bit codes, for gfx950.
+// H2O decode step over a cache stored as 8-, 4- or 2-bit codes, for gfx950.
 //
 // Citations ("H2O §x") refer to the page "H2O: Heavy-Hitter Oracle for
 // Efficient Generative Inference of Large Language Models" (paperlayer.ai
@@ -16,33 +16,16 @@
 //             so each head pre-scales q by the key grid once and adds one bias;
 //   p_a v_a = (p_a s_a) code_a + (p_a mn_a) 1, so the P.V accumulator takes
 //             p_a s_a per row and a separate sum of p_a mn_a.
-// A row of d codes is read by d/16 lanes (16 codes each), one wave per head,
-// persistent over heads, two batches of rows in flight as in the wave kernel
-// of decode.hip. The new token's key and value are quantised on insert.
+// A row of d codes is read by d/16 lanes (16 codes, 2 * BITS bytes, each),
+// one wave per head, persistent over heads, two batches of rows in flight as
+// in the wave kernel of decode.hip; narrower codes take more rows per batch.
+// The new token's key and value are quantised on insert.
 
 #include "h2o_device.h"
 #include "launch.h"
 
 namespace h2o {
 namespace {
-
-__device__ __forceinline__ void codes_to_float(uint4 w, float (&c)[16]) {
-  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c[4 * i] = float(v[i] & 0xFFu);
-    c[4 * i + 1] = float((v[i] >> 8) & 0xFFu);
-    c[4 * i + 2] = float((v[i] >> 16) & 0xFFu);
-    c[4 * i + 3] = float(v[i] >> 24);
-  }
-}
-
-__device__ __forceinline__ uint4 pack_codes(const uint32_t (&c)[16]) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = c[4 * i] | c[4 * i + 1] << 8 | c[4 * i + 2] << 16 | c[4 * i + 3] << 24;
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 // 16 consecutive elements of a dtype row: raw 16-byte chunks, then fp32.
 template <int DT> struct Raw16 {
@@ -60,12 +43,16 @@ template <int DT> struct Raw16 {
 };
 
 // One wave per head.
-//   UB: wave-loads of codes (1 KiB of K and 1 KiB of V) per batch; PF: score/pos
-//   entries per lane prefetched with the head's inputs.
-template <int DT, int D, int UB, int PF>
-__global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
-  constexpr int LPR = D / 16;    // lanes per row of codes
-  constexpr int RPU = 64 / LPR;  // rows per wave-wide load
+//   BITS: code width; UB: wave-loads of codes (K and V, 128 * BITS bytes each)
+//   per batch; PF: score/pos entries per lane prefetched with the head's inputs.
+template <int DT, int D, int BITS, int UB, int PF>
+__global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G) {
+  using LC = LaneCodes<BITS>;
+  using CT = typename LC::T;
+  constexpr int LPR = D / 16;          // lanes per row of codes
+  constexpr int RPU = 64 / LPR;        // rows per wave-wide load
+  constexpr int RB = D * BITS / 8;     // bytes per code row
+  constexpr int CB = 2 * BITS;         // code bytes per lane
   extern __shared__ float sm_logit[];  // [k] logits of the current head, base-2 units
   const int lane = threadIdx.x;
   const int grp = lane / LPR;
@@ -110,7 +97,7 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
     // The new token's codes do not depend on the step's attention, only the
     // slot they go to does: quantise now, while the first rows are in flight
     // (32 correctly rounded divisions per lane off the epilogue's path).
-    uint4 kn_codes, vn_codes;
+    CT kn_codes, vn_codes;
     float vs, vmn;
     {
       float kn[16], vn[16];
@@ -125,15 +112,15 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
       }
       vmn = lane_group<LPR>(vmn, OpMin());
       vmx = lane_group<LPR>(vmx, OpMax());
-      vs = u8_grid_scale(vmn, vmx);
+      vs = grid_scale<BITS>(vmn, vmx);
       uint32_t kc[16], vc[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        kc[i] = quantize_u8(kn[i], ks[i], km[i]);
-        vc[i] = quantize_u8(vn[i], vs, vmn);
+        kc[i] = quantize_code<BITS>(kn[i], ks[i], km[i]);
+        vc[i] = quantize_code<BITS>(vn[i], vs, vmn);
       }
-      kn_codes = pack_codes(kc);
-      vn_codes = pack_codes(vc);
+      kn_codes = LC::pack(kc);
+      vn_codes = LC::pack(vc);
     }
     float sc_pf[PF];
     int pos_pf[PF];
@@ -149,8 +136,8 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
     }
 
     // ---- stream the codes: per lane-group online softmax -------------------------------
-    const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * D + c0;
-    const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * D + c0;
+    const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * RB + sub * CB;
+    const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * RB + sub * CB;
     const float2* vg = reinterpret_cast<const float2*>(a.v_qparam) + hrow;
     float m = kNegInf, l = 0.f, pm = 0.f;  // pm: sum of p * value-grid minimum
     float acc[16];
@@ -158,23 +145,23 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
     // Loads are unconditional (clamped to the last occupied row, masked) so
     // that the compiler's wait counts stay exact.
-    auto issue = [&](uint4 (&kb)[UB], uint4 (&vb)[UB], float2 (&gb)[UB], int b) {
+    auto issue = [&](CT (&kb)[UB], CT (&vb)[UB], float2 (&gb)[UB], int b) {
 #pragma unroll
       for (int j = 0; j < UB; ++j) {
         const int row = min((b * UB + j) * RPU + grp, nu - 1);
-        kb[j] = ld16(Kh + size_t(row) * D);
-        vb[j] = ld16(Vh + size_t(row) * D);
+        kb[j] = LC::load(Kh + size_t(row) * RB);
+        vb[j] = LC::load(Vh + size_t(row) * RB);
         gb[j] = vg[row];
       }
     };
-    auto compute = [&](const uint4 (&kb)[UB], const uint4 (&vb)[UB], const float2 (&gb)[UB], int b) {
+    auto compute = [&](const CT (&kb)[UB], const CT (&vb)[UB], const float2 (&gb)[UB], int b) {
       float s[UB];
       float bm = kNegInf;
 #pragma unroll
       for (int j = 0; j < UB; ++j) {
         const int row = (b * UB + j) * RPU + grp;
         float c[16];
-        codes_to_float(kb[j], c);
+        LC::to_float(kb[j], c);
         float x4[4] = {0.f, 0.f, 0.f, 0.f};  // four short chains instead of one long one
 #pragma unroll
         for (int i = 0; i < 16; ++i) x4[i % 4] = fmaf(qs[i], c[i], x4[i % 4]);
@@ -197,7 +184,7 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
           pm = fmaf(p, gb[j].y, pm);
           const float ps = p * gb[j].x;
           float c[16];
-          codes_to_float(vb[j], c);
+          LC::to_float(vb[j], c);
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[i] = fmaf(ps, c[i], acc[i]);
         }
@@ -205,7 +192,7 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
       }
     };
     if (nb > 0) {
-      uint4 kA[UB], vA[UB], kB[UB], vB[UB];
+      CT kA[UB], vA[UB], kB[UB], vB[UB];
       float2 gA[UB], gB[UB];
       issue(kA, vA, gA, 0);
       for (int b = 0; b < nb; b += 2) {
@@ -314,8 +301,8 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
         pos_g[victim] = a.t;
       }
       if (grp == 0) {
-        st16(static_cast<uint8_t*>(a.K_w) + (hrow + victim) * D + c0, kn_codes);
-        st16(static_cast<uint8_t*>(a.V_w) + (hrow + victim) * D + c0, vn_codes);
+        LC::store(static_cast<uint8_t*>(a.K_w) + (hrow + victim) * RB + sub * CB, kn_codes);
+        LC::store(static_cast<uint8_t*>(a.V_w) + (hrow + victim) * RB + sub * CB, vn_codes);
         if (sub == 0) reinterpret_cast<float2*>(a.v_qparam)[hrow + victim] = make_float2(vs, vmn);
       }
     }
@@ -323,27 +310,39 @@ __global__ __launch_bounds__(64, 2) void decode_u8_kernel(DecodeArgs a, int G) {
   }
 }
 
-template <int DT, int D>
+template <int DT, int D, int BITS>
 hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
-  constexpr int UB = 2, PF = 4, MINW = 2;
+  // K and V codes per batch: 2 KiB at 8 and 4 bits (2 or 4 wave-loads), 1 KiB
+  // at 2 bits (4 wave-loads; 8 would spill registers).
+  constexpr int UB = BITS == 8 ? 2 : 4, PF = 4, MINW = 2;
   const int resident = cu_count() * 4 * MINW;
   const int grid = G < resident ? G : resident;
   const size_t shmem = size_t(a.k) * sizeof(float);
-  hipLaunchKernelGGL((decode_u8_kernel<DT, D, UB, PF>), dim3(grid), dim3(64), shmem, s, a, G);
+  hipLaunchKernelGGL((decode_quant_kernel<DT, D, BITS, UB, PF>), dim3(grid), dim3(64), shmem, s, a, G);
   return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t dispatch(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s) {
+  switch (dtype * 1000 + head_dim) {
+    case DT_F32 * 1000 + 64: return launch_typed<DT_F32, 64, BITS>(G, a, s);
+    case DT_F32 * 1000 + 128: return launch_typed<DT_F32, 128, BITS>(G, a, s);
+    case DT_BF16 * 1000 + 64: return launch_typed<DT_BF16, 64, BITS>(G, a, s);
+    case DT_BF16 * 1000 + 128: return launch_typed<DT_BF16, 128, BITS>(G, a, s);
+    case DT_F16 * 1000 + 64: return launch_typed<DT_F16, 64, BITS>(G, a, s);
+    case DT_F16 * 1000 + 128: return launch_typed<DT_F16, 128, BITS>(G, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_decode_u8(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_quant(int bits, int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s) {
   if (G <= 0) return hipSuccess;
-  switch (dtype * 1000 + head_dim) {
-    case DT_F32 * 1000 + 64: return launch_typed<DT_F32, 64>(G, a, s);
-    case DT_F32 * 1000 + 128: return launch_typed<DT_F32, 128>(G, a, s);
-    case DT_BF16 * 1000 + 64: return launch_typed<DT_BF16, 64>(G, a, s);
-    case DT_BF16 * 1000 + 128: return launch_typed<DT_BF16, 128>(G, a, s);
-    case DT_F16 * 1000 + 64: return launch_typed<DT_F16, 64>(G, a, s);
-    case DT_F16 * 1000 + 128: return launch_typed<DT_F16, 128>(G, a, s);
+  switch (bits) {
+    case 8: return dispatch<8>(dtype, head_dim, G, a, s);
+    case 4: return dispatch<4>(dtype, head_dim, G, a, s);
+    case 2: return dispatch<2>(dtype, head_dim, G, a, s);
     default: return hipErrorInvalidValue;
   }
 }

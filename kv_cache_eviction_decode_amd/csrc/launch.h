@@ -23,8 +23,8 @@ struct DecodeArgs {
   const void* v_new;   // [G][d]           (scored mode only)
   float* out;          // [G][d] fp32
   int32_t* evicted;    // [G]              (scored mode only)
-  const float* k_qparam;  // [G][2][d] key grids (8-bit caches only)
-  float* v_qparam;        // [G][k][2] value grids (8-bit caches only)
+  const float* k_qparam;  // [G][2][d] key grids (caches stored as codes only)
+  float* v_qparam;        // [G][k][2] value grids (caches stored as codes only)
   int32_t k;           // slot capacity (rows per head in K/V)
   int32_t n_used;      // occupied slots [0, n_used), or full-cache length
   int32_t t;           // position of the new token
@@ -40,8 +40,9 @@ int cu_count();
 // accumulation, at most one eviction, insert. One workgroup per head.
 hipError_t launch_decode(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);
 
-// Decode step of a cache stored as 8-bit codes (K, V point to the codes).
-hipError_t launch_decode_u8(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);
+// Decode step of a cache stored as bits-wide codes, bits in {8, 4, 2} (K, V
+// point to the packed codes).
+hipError_t launch_decode_quant(int bits, int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);
 
 // Split decode: the occupied slots of every head are cut into `chunks` runs of
 // `chunk_len` rows (the last one ragged), each streamed by its own wave; a

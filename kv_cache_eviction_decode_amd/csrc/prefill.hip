@@ -24,6 +24,7 @@
 // recent window (H2O §A "Pseudocode", "System Details") and copies the K/V
 // rows into the cache slots.
 
+#include "../../include/h2o.h"
 #include "h2o_device.h"
 #include "launch.h"
 #include "prefill_launch.h"
@@ -637,17 +638,22 @@ __device__ int block_exclusive_scan(int v, int* sm_wave, int& total) {
   return before + x - v;
 }
 
-template <int N> __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&c)[N]) {
-  static_assert(N == 4 || N == 8, "4 or 8 codes");
-  uint32_t w[N / 4];
+// N consecutive BITS-wide codes (the first channel a multiple of 8 / BITS),
+// packed low bits first into N * BITS / 8 bytes (1 to 8).
+template <int N, int BITS> __device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&c)[N]) {
+  static_assert((N == 4 || N == 8) && (BITS == 8 || BITS == 4 || BITS == 2), "4 or 8 codes of 8, 4 or 2 bits");
+  uint64_t w = 0;
 #pragma unroll
-  for (int i = 0; i < N / 4; ++i)
-    w[i] = c[4 * i] | c[4 * i + 1] << 8 | c[4 * i + 2] << 16 | c[4 * i + 3] << 24;
-  if constexpr (N == 4) *reinterpret_cast<uint32_t*>(p) = w[0];
-  else *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  for (int i = 0; i < N; ++i) w |= uint64_t(c[i]) << (BITS * i);
+  constexpr int bytes = N * BITS / 8;
+  if constexpr (bytes == 8) *reinterpret_cast<uint2*>(p) = make_uint2(uint32_t(w), uint32_t(w >> 32));
+  else if constexpr (bytes == 4) *reinterpret_cast<uint32_t*>(p) = uint32_t(w);
+  else if constexpr (bytes == 2) *reinterpret_cast<uint16_t*>(p) = uint16_t(w);
+  else *p = uint8_t(w);
 }
 
-template <int DT, int D, bool QUANT>
+// BITS = 0: the cache holds rows in the input dtype; 8, 4, 2: packed codes.
+template <int DT, int D, int BITS>
 __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
   constexpr int E = Elem<DT>::bytes, ROW = D * E, LPR = ROW / 16;
   __shared__ int slot_pos[8192];
@@ -745,10 +751,12 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
   const int sub = tid % LPR;
   const char* Kp = static_cast<const char*>(a.K) + size_t(head) * n * ROW + sub * 16;
   const char* Vp = static_cast<const char*>(a.V) + size_t(head) * n * ROW + sub * 16;
-  if constexpr (QUANT) {
-    // 8-bit cache: each lane quantises its EPL elements of the row; keys on
-    // the head's channel grids, values on the row's own grid.
+  if constexpr (BITS > 0) {
+    // Codes: each lane quantises its EPL elements of the row; keys on the
+    // head's channel grids, values on the row's own grid.
     constexpr int EPL = 16 / E;
+    constexpr int RB = D * BITS / 8;          // bytes per code row
+    constexpr int LB = EPL * BITS / 8;        // code bytes per lane
     const float* kg = a.kq_param + size_t(head) * 2 * D + sub * EPL;
     float ks[EPL], km[EPL];
 #pragma unroll
@@ -756,8 +764,8 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
       ks[e] = kg[e];
       km[e] = kg[D + e];
     }
-    uint8_t* cK = static_cast<uint8_t*>(a.cK) + hk * D + sub * EPL;
-    uint8_t* cV = static_cast<uint8_t*>(a.cV) + hk * D + sub * EPL;
+    uint8_t* cK = static_cast<uint8_t*>(a.cK) + hk * RB + sub * LB;
+    uint8_t* cV = static_cast<uint8_t*>(a.cV) + hk * RB + sub * LB;
     for (int s = tid / LPR; s < filled; s += kSelThreads / LPR) {
       const int p = slot_pos[s];
       if (p < 0 || p >= n) continue;  // cannot happen for a consistent selection
@@ -767,7 +775,7 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
       Unpack<DT>::run(ld16(Vp + src), v);
       uint32_t kc[EPL], vc[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) kc[e] = quantize_u8(x[e], ks[e], km[e]);
+      for (int e = 0; e < EPL; ++e) kc[e] = quantize_code<BITS>(x[e], ks[e], km[e]);
       float vmn = v[0], vmx = v[0];
 #pragma unroll
       for (int e = 1; e < EPL; ++e) {
@@ -776,11 +784,11 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
       }
       vmn = lane_group<LPR>(vmn, OpMin());
       vmx = lane_group<LPR>(vmx, OpMax());
-      const float vs = u8_grid_scale(vmn, vmx);
+      const float vs = grid_scale<BITS>(vmn, vmx);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) vc[e] = quantize_u8(v[e], vs, vmn);
-      store_codes<EPL>(cK + size_t(s) * D, kc);
-      store_codes<EPL>(cV + size_t(s) * D, vc);
+      for (int e = 0; e < EPL; ++e) vc[e] = quantize_code<BITS>(v[e], vs, vmn);
+      store_codes<EPL, BITS>(cK + size_t(s) * RB, kc);
+      store_codes<EPL, BITS>(cV + size_t(s) * RB, vc);
       if (sub == 0) *reinterpret_cast<float2*>(a.vq_param + (hk + s) * 2) = make_float2(vs, vmn);
     }
   } else {
@@ -796,9 +804,10 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
   }
 }
 
-// Key grids of an 8-bit cache: per (head, channel), the smallest and largest
-// prompt key, scale = (mx - mn) / 255. One workgroup per head.
-template <int DT, int D>
+// Key grids of a cache stored as BITS-wide codes: per (head, channel), the
+// smallest and largest prompt key, scale = (mx - mn) / (2^BITS - 1). One
+// workgroup per head.
+template <int DT, int D, int BITS>
 __global__ __launch_bounds__(256) void key_grid(PrefillArgs a) {
   constexpr int E = Elem<DT>::bytes, ROW = D * E, LPR = ROW / 16, EPL = 16 / E, RPP = 256 / LPR;
   __shared__ float sm_mn[RPP][D + 1];
@@ -835,7 +844,7 @@ __global__ __launch_bounds__(256) void key_grid(PrefillArgs a) {
       hi = fmaxf(hi, sm_mx[i][c]);
     }
     float* kg = a.kq_param + size_t(head) * 2 * D;
-    kg[c] = u8_grid_scale(lo, hi);
+    kg[c] = grid_scale<BITS>(lo, hi);
     kg[D + c] = lo;
   }
 }
@@ -873,11 +882,24 @@ hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((rowattn8_lds<DT, D>), dim3(grid), dim3(512), 0, s, a, nblk, G, ld_lse);
     hipLaunchKernelGGL((colsum_lds<DT, D>), dim3(grid), dim3(256), 0, s, a, nblk, G, ld_lse);
   }
-  if (a.quant) {
-    hipLaunchKernelGGL((key_grid<DT, D>), dim3(G), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((select_gather<DT, D, true>), dim3(G), dim3(kSelThreads), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((select_gather<DT, D, false>), dim3(G), dim3(kSelThreads), 0, s, a);
+  switch (a.quant) {
+    case H2O_QUANT_NONE:
+      hipLaunchKernelGGL((select_gather<DT, D, 0>), dim3(G), dim3(kSelThreads), 0, s, a);
+      break;
+    case H2O_QUANT_U8:
+      hipLaunchKernelGGL((key_grid<DT, D, 8>), dim3(G), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((select_gather<DT, D, 8>), dim3(G), dim3(kSelThreads), 0, s, a);
+      break;
+    case H2O_QUANT_U4:
+      hipLaunchKernelGGL((key_grid<DT, D, 4>), dim3(G), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((select_gather<DT, D, 4>), dim3(G), dim3(kSelThreads), 0, s, a);
+      break;
+    case H2O_QUANT_U2:
+      hipLaunchKernelGGL((key_grid<DT, D, 2>), dim3(G), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((select_gather<DT, D, 2>), dim3(G), dim3(kSelThreads), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -25,6 +25,7 @@ import torch
 
 from kv_cache_eviction_decode_amd import H2OCache
 from oracle import H2OOracle
+from oracle import quant as qz
 from oracle.h2o_oracle import prefill_attention, retention_value
 from workload import Workload, make_decode, make_prompt
 
@@ -123,23 +124,23 @@ class ParityRun:
             self._write_sampled(self.cache.pos, self.orc.pos.astype(np.int32), heads_full)
             if self.quant:
                 o = self.orc
-                self._write_sampled(self.cache.K, o.Kq, heads_full)
-                self._write_sampled(self.cache.V, o.Vq, heads_full)
+                self._write_sampled(self.cache.K, qz.pack(o.Kq, o.bits), heads_full)
+                self._write_sampled(self.cache.V, qz.pack(o.Vq, o.bits), heads_full)
                 self._write_sampled(self.cache.v_qparam, np.stack([o.v_scale, o.v_min], -1), heads_full)
             else:
                 self._write_sampled(self.cache.K, self.orc.K.astype(np.float32), heads_full)
                 self._write_sampled(self.cache.V, self.orc.V.astype(np.float32), heads_full)
 
     def _check_codes(self, same):
-        """8-bit cache: codes and grids of the heads that agree, bit for bit."""
+        """Cache of codes: packed codes and grids of the heads that agree, bit for bit."""
         if not self.quant or not same.any():
             return
         o = self.orc
         gK, gV = self._gpu_sampled(self.cache.K), self._gpu_sampled(self.cache.V)
         gvq = self._gpu_sampled(self.cache.v_qparam)
         live = (o.pos >= 0)[same]
-        assert np.array_equal(gK[same][live], o.Kq[same][live]), "key codes differ"
-        assert np.array_equal(gV[same][live], o.Vq[same][live]), "value codes differ"
+        assert np.array_equal(gK[same][live], qz.pack(o.Kq, o.bits)[same][live]), "key codes differ"
+        assert np.array_equal(gV[same][live], qz.pack(o.Vq, o.bits)[same][live]), "value codes differ"
         assert np.array_equal(gvq[same][live], np.stack([o.v_scale, o.v_min], -1)[same][live]), \
             "value grids differ"
 

@@ -81,6 +81,32 @@ def test_u8_init_rejects_missing_grids():
     assert st == b.H2O_EINVAL and "k_qparam" in b.h2o_last_error() and d.magic == 0
 
 
+@pytest.mark.parametrize("quant", [b.H2O_QUANT_U8, b.H2O_QUANT_U4, b.H2O_QUANT_U2])
+def test_quant_init_rejects_missing_grids(quant):
+    lib = b.load_library()
+    d = b.h2o_cache()
+    st = lib.h2o_cache_init_quant(ctypes.byref(d), 1, 1, 128, 4, 4, 0, 1, 0.1, quant, None, None, None, None,
+                                  None, None, None)
+    assert st == b.H2O_EINVAL and "k_qparam" in b.h2o_last_error() and d.magic == 0
+
+
+@pytest.mark.parametrize("quant", [b.H2O_QUANT_NONE, 4, -1])
+def test_quant_init_rejects_unknown_format(quant):
+    lib = b.load_library()
+    d = b.h2o_cache()
+    st = lib.h2o_cache_init_quant(ctypes.byref(d), 1, 1, 128, 4, 4, 0, 1, 0.1, quant, None, None, None, None,
+                                  None, None, None)
+    assert st == b.H2O_EINVAL and "code format" in b.h2o_last_error() and d.magic == 0
+
+
+def test_quant_constants_match_header():
+    import re
+    text = open(b.HEADER).read()
+    vals = {m.group(1): int(m.group(2)) for m in re.finditer(r"(H2O_QUANT_\w+)\s*=\s*(\d+)", text)}
+    assert vals == {"H2O_QUANT_NONE": b.H2O_QUANT_NONE, "H2O_QUANT_U8": b.H2O_QUANT_U8,
+                    "H2O_QUANT_U4": b.H2O_QUANT_U4, "H2O_QUANT_U2": b.H2O_QUANT_U2}
+
+
 def test_calls_on_uninitialised_cache_are_rejected():
     lib = b.load_library()
     d = b.h2o_cache()

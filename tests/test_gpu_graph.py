@@ -41,14 +41,14 @@ def _load(c, snap):
         dst.copy_(src)
 
 
-@pytest.mark.parametrize("mode", ["fused", "split", "u8"])
+@pytest.mark.parametrize("mode", ["fused", "split", "u8", "u4", "u2"])
 def test_decode_steps_replay_from_a_graph(gpu, mode):
     wl = Workload("graph_" + mode, 2, 4, 128, "bf16", 300, 24, 24, T, 1.5, 0.0, seed=55)
     dev = torch.device("cuda")
     P, D = _inputs(wl, dev)
     B, H, d = wl.batch, wl.heads, wl.head_dim
     c = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, torch.bfloat16, wl.scale, dev,
-                 quant="u8" if mode == "u8" else None)
+                 quant=mode if mode in ("u8", "u4", "u2") else None)
     c.prefill_select(*P)
     outs = torch.empty(T, B, H, d, dtype=torch.float32, device=dev)
     evs = torch.empty(T, B, H, dtype=torch.int32, device=dev)

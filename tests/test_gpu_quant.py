@@ -1,7 +1,8 @@
-"""GPU parity of the 8-bit cache (h2o_cache_init_u8) against the fp64 oracle's
-quantised mode, through the C ABI.
+"""GPU parity of the caches stored as 8-, 4- and 2-bit codes
+(h2o_cache_init_quant) against the fp64 oracle's quantised modes, through the
+C ABI.
 
-Codes and grids of every cached row are compared bit for bit (both sides
+Packed codes and grids of every cached row are compared bit for bit (both sides
 take each rounding decision with the same fp32 operations); outputs, scores,
 selections and evictions to the same tolerances as the plain cache. Cases
 span both head sizes, every input dtype, ragged prompts, a cache still
@@ -32,30 +33,37 @@ QUANT_CASES = [
 ]
 
 
+FORMATS = ["u8", "u4", "u2"]
+
+
+@pytest.mark.parametrize("quant", FORMATS)
 @pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
-def test_u8_parity(gpu, case):
+def test_quant_parity(gpu, case, quant):
     name, policy, B, H, d, dt, n, kh, kr, T, sink = case
-    wl = Workload("u8_" + name, B, H, d, dt, n, kh, kr, T, 1.5, sink, seed=zlib.crc32(name.encode()) % 10000)
-    run = ParityRun(wl, T, policy=policy, quant="u8")
+    wl = Workload(f"{quant}_" + name, B, H, d, dt, n, kh, kr, T, 1.5, sink,
+                  seed=zlib.crc32(name.encode()) % 10000)
+    run = ParityRun(wl, T, policy=policy, quant=quant)
     run.prefill()
     rep = run.decode()
-    log(f"[u8] {name} ({policy}): {rep}")
+    log(f"[{quant}] {name} ({policy}): {rep}")
     assert rep.steps == T
 
 
-def test_u8_opt_layer_full_size(gpu):
+@pytest.mark.parametrize("quant", FORMATS)
+def test_quant_opt_layer_full_size(gpu, quant):
     """The OPT-6.7B layer shape (2048 heads x 256 slots), as in the benchmark."""
     wl = WORKLOADS["opt6.7b_layer"]
-    run = ParityRun(wl, 64, sample=sample_heads(wl, 16), quant="u8")
+    run = ParityRun(wl, 64, sample=sample_heads(wl, 16), quant=quant)
     run.prefill()
     rep = run.decode()
-    log(f"[u8] opt6.7b_layer full size: {rep}")
+    log(f"[{quant}] opt6.7b_layer full size: {rep}")
     assert rep.steps == 64
 
 
-def test_u8_errors(gpu):
+@pytest.mark.parametrize("quant", FORMATS)
+def test_quant_errors(gpu, quant):
     from kv_cache_eviction_decode_amd import H2OCache, binding as b
-    c = H2OCache(1, 2, 128, 8, 8, torch.bfloat16, device="cuda", quant="u8")
+    c = H2OCache(1, 2, 128, 8, 8, torch.bfloat16, device="cuda", quant=quant)
     z = torch.zeros(1, 2, 0, 128, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(b.H2OError, match="at least one token"):
         c.prefill_select(z, z, z)
