@@ -63,7 +63,8 @@ def parse_args():
     p.add_argument("--quant", choices=("none", "u8", "u4", "u2"), default="none",
                    help="cache storage: rows in the workload dtype, or 8-, 4- or 2-bit codes "
                         "(h2o_cache_init_quant)")
-    p.add_argument("--cpu-heads", type=int, default=256, help="heads in the CPU-oracle sample")
+    p.add_argument("--cpu-heads", type=int, default=0,
+                   help="heads in the CPU-oracle sample (0: enough for about 15 s of oracle work)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-single-layer", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -109,13 +110,21 @@ def load_traffic(workload: str, digest: str, mode: str = "fused"):
     return rec.get("bytes_per_launch")
 
 
+def cpu_sample_heads(wl, seconds: float = 15.0) -> int:
+    """Heads whose oracle prefill and decode take about `seconds` on 16 host
+    threads (per-head cost measured on the OPT-6.7B layer: 46 ps per n^2 d of
+    prefill, 0.55 ns per step x slot x channel of decode)."""
+    per_head = 4.6e-11 * wl.prompt_len ** 2 * wl.head_dim + 5.5e-10 * wl.steps * wl.k * wl.head_dim
+    return int(max(1, min(wl.n_heads_total, round(seconds / per_head))))
+
+
 def cpu_baseline(wl, heads: int):
     """The fp64 oracle on a bounded sample: `heads` heads, prefill plus every decode step."""
     import numpy as np
     from oracle import H2OOracle
     from workload import make_decode, make_prompt, sample_heads
 
-    sample = sample_heads(wl, heads, seed=11)
+    sample = sample_heads(wl, heads or cpu_sample_heads(wl), seed=11)
     Q, K, V = make_prompt(wl, heads=sample)
     q, k, v = make_decode(wl, heads=sample)
     try:
@@ -276,6 +285,9 @@ def main():
     avg_launch_s = (sum(decode_ms) / args.steps) / 1e3 / launches
     achieved = bytes_per_launch / avg_launch_s / 1e9
     mode = args.quant if quant else args.decode
+    # the library runs one wave per head when the heads fill half the resident waves (2 per SIMD)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    fused_kernel = "decode_wave_kernel" if G >= cus * 4 else "decode_kernel"
     digest = decode_source_digest(mode)
     traffic = load_traffic(wl.name, digest, mode) if args.batch is None and args.heads is None else None
     # two causal QK^T passes per layer (d n (n+1) flops each), plus the causal P.V with the output
@@ -319,7 +331,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ("h2o decode_chunk_kernel + decode_merge_kernel (split decode)" if split else
                                 f"h2o decode_quant_kernel (fused step over {args.quant} codes)" if quant else
-                                "h2o decode_kernel (fused attention + score + evict + insert)"),
+                                f"h2o {fused_kernel} (fused attention + score + evict + insert)"),
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
                      "kernel_source_digest": digest},
         "decode_head_steps_per_s": head_steps / (sum(decode_ms) / args.steps / 1e3),
