@@ -102,8 +102,8 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_kernel(DecodeArgs a) 
       kr[j] = make_uint4(0, 0, 0, 0);
       vr[j] = make_uint4(0, 0, 0, 0);
       if (row[j] < nu) {
-        kr[j] = ld16(Kh + size_t(row[j]) * S::ROW);
-        vr[j] = ld16(Vh + size_t(row[j]) * S::ROW);
+        kr[j] = ldnt16(Kh + size_t(row[j]) * S::ROW);
+        vr[j] = ldnt16(Vh + size_t(row[j]) * S::ROW);
       }
     }
     float s[UB];
@@ -329,8 +329,8 @@ __global__ __launch_bounds__(64, MINW) void decode_wave_kernel(DecodeArgs a, int
 #pragma unroll
     for (int j = 0; j < UB; ++j) {
       const int row = min((b * UB + j) * S::RPU + grp, nu - 1);
-      kb[j] = ld16(Kh + size_t(row) * S::ROW);
-      vb[j] = ld16(Vh + size_t(row) * S::ROW);
+      kb[j] = ldnt16(Kh + size_t(row) * S::ROW);
+      vb[j] = ldnt16(Vh + size_t(row) * S::ROW);
     }
   };
 

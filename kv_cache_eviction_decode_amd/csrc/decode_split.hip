@@ -65,8 +65,8 @@ __global__ __launch_bounds__(64, 2) void decode_chunk_kernel(DecodeArgs a, Split
 #pragma unroll
     for (int j = 0; j < UB; ++j) {
       const int row = min(r0 + (b * UB + j) * S::RPU + grp, r1 - 1);
-      kb[j] = ld16(Kh + size_t(row) * S::ROW);
-      vb[j] = ld16(Vh + size_t(row) * S::ROW);
+      kb[j] = ldnt16(Kh + size_t(row) * S::ROW);
+      vb[j] = ldnt16(Vh + size_t(row) * S::ROW);
     }
   };
   float m = kNegInf, l = 0.f;
