@@ -771,8 +771,8 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
       if (p < 0 || p >= n) continue;  // cannot happen for a consistent selection
       const size_t src = size_t(p) * ROW;
       float x[EPL], v[EPL];
-      Unpack<DT>::run(ld16(Kp + src), x);
-      Unpack<DT>::run(ld16(Vp + src), v);
+      Unpack<DT>::run(ldnt16(Kp + src), x);
+      Unpack<DT>::run(ldnt16(Vp + src), v);
       uint32_t kc[EPL], vc[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) kc[e] = quantize_code<BITS>(x[e], ks[e], km[e]);
@@ -798,8 +798,8 @@ __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
       const int p = slot_pos[s];
       if (p < 0 || p >= n) continue;  // cannot happen for a consistent selection
       const size_t src = size_t(p) * ROW;
-      st16(cK + size_t(s) * ROW, ld16(Kp + src));
-      st16(cV + size_t(s) * ROW, ld16(Vp + src));
+      st16(cK + size_t(s) * ROW, ldnt16(Kp + src));
+      st16(cV + size_t(s) * ROW, ldnt16(Vp + src));
     }
   }
 }
