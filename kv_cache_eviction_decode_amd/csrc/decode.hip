@@ -25,7 +25,7 @@
 //   decode_wave_kernel - one wave per head, persistent, double-buffered, all
 //     reductions inside the wave (DPP, v_permlane*_swap); used when there are
 //     enough heads to give every SIMD at least one wave.
-//   decode_kernel      - one 4-wave workgroup per head with an LDS merge; used
+//   decode_kernel      - one 8-wave workgroup per head with an LDS merge; used
 //     for few heads with long caches.
 
 #include "h2o_device.h"
@@ -520,11 +520,12 @@ hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
     const int grid = G < resident ? G : resident;
     hipLaunchKernelGGL((decode_wave_kernel<DT, D, UB, PF, WMINW, SCORED>), dim3(grid), dim3(64), shmem, s, a, G);
   } else {
-    // Few heads: spread each head over a 4-wave workgroup instead. With a
-    // workgroup per CU or more, 4-deep batches are 4% faster than 8 (256
-    // heads x 2048 slots); with fewer, each workgroup needs the deeper batches
-    // to keep enough bytes in flight (32 heads: 33 us against 39).
-    constexpr int WAVES = 4, PF = 4, MINW = 1;
+    // Few heads: spread each head over an 8-wave workgroup instead (two
+    // waves per SIMD; against 4 waves: 32 heads x 2048 slots 33.5 -> 23.8 us,
+    // 256 heads 46.5 -> 44.4 us; 16 waves is slower). With a workgroup per
+    // CU or more, 4-deep batches are best; with fewer, each workgroup needs
+    // the deeper batches to keep enough bytes in flight.
+    constexpr int WAVES = 8, PF = 4, MINW = 2;
     if (G >= cu_count())
       hipLaunchKernelGGL((decode_kernel<DT, D, WAVES, 4, PF, MINW, SCORED>), dim3(G), dim3(WAVES * 64), shmem, s, a);
     else
