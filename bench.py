@@ -288,6 +288,7 @@ def main():
     # the library runs one wave per head when the heads fill half the resident waves (2 per SIMD)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     fused_kernel = "decode_wave_kernel" if G >= cus * 4 else "decode_kernel"
+    quant_kernel = "decode_quant_kernel" if G >= cus * 4 else "decode_quant_wg_kernel"
     digest = decode_source_digest(mode)
     traffic = load_traffic(wl.name, digest, mode) if args.batch is None and args.heads is None else None
     # two causal QK^T passes per layer (d n (n+1) flops each), plus the causal P.V with the output
@@ -330,7 +331,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ("h2o decode_chunk_kernel + decode_merge_kernel (split decode)" if split else
-                                f"h2o decode_quant_kernel (fused step over {args.quant} codes)" if quant else
+                                f"h2o {quant_kernel} (fused step over {args.quant} codes)" if quant else
                                 f"h2o {fused_kernel} (fused attention + score + evict + insert)"),
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
                      "kernel_source_digest": digest},

@@ -18,7 +18,8 @@
 //             p_a s_a per row and a separate sum of p_a mn_a.
 // A row of d codes is read by d/16 lanes (16 codes, 2 * BITS bytes, each),
 // one wave per head, persistent over heads, two batches of rows in flight as
-// in the wave kernel of decode.hip; narrower codes take more rows per batch.
+// in the wave kernel of decode.hip (an 8-wave workgroup per head when there
+// are few heads); narrower codes take more rows per batch.
 // The new token's key and value are quantised on insert.
 
 #include "h2o_device.h"
@@ -310,15 +311,341 @@ __global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G
   }
 }
 
+// Few heads: one WAVES-wave workgroup per head. Wave w streams units w,
+// w + WAVES, ... of the head's rows with the same per-lane-group online
+// softmax as the wave kernel; each wave merges its lane groups, the waves'
+// partials are merged through LDS, and all threads share the score update
+// and the victim search (per-wave minima, then a minimum over the waves).
+template <int DT, int D, int BITS, int WAVES, int UB, int PF>
+__global__ __launch_bounds__(WAVES * 64, 2) void decode_quant_wg_kernel(DecodeArgs a) {
+  using LC = LaneCodes<BITS>;
+  using CT = typename LC::T;
+  constexpr int LPR = D / 16;
+  constexpr int RPU = 64 / LPR;
+  constexpr int RB = D * BITS / 8;
+  constexpr int CB = 2 * BITS;
+  constexpr int NT = WAVES * 64;
+  extern __shared__ float sm_logit[];  // [k] logits of the head, base-2 units
+  __shared__ float sm_m[WAVES], sm_l[WAVES], sm_pm[WAVES];
+  __shared__ __attribute__((aligned(16))) float sm_acc[WAVES][D];
+  __shared__ uint64_t sm_key[WAVES];
+  __shared__ int sm_slot[WAVES], sm_epos[WAVES];
+
+  const int head = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane / LPR, sub = lane % LPR;
+  const int c0 = sub * 16;
+  const int nu = a.n_used;
+  const size_t hrow = size_t(head) * a.k;
+  const size_t hoff = size_t(head) * D * Elem<DT>::bytes;
+
+  // ---- head inputs: q folded with the key grid, the new token, scores -----------------
+  Raw16<DT> q_raw, kn_raw, vn_raw;
+  q_raw.load(static_cast<const char*>(a.q) + hoff, c0);
+  kn_raw.load(static_cast<const char*>(a.k_new) + hoff, c0);
+  vn_raw.load(static_cast<const char*>(a.v_new) + hoff, c0);
+  const float4* kg4 = reinterpret_cast<const float4*>(a.k_qparam + size_t(head) * 2 * D + c0);
+  float4 ks4[4], km4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ks4[i] = kg4[i];
+    km4[i] = kg4[D / 4 + i];
+  }
+  const float* ks = reinterpret_cast<const float*>(ks4);
+  const float* km = reinterpret_cast<const float*>(km4);
+  float qs[16];
+  float bias;
+  {
+    float q[16];
+    q_raw.unpack(q);
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      qs[i] = q[i] * ks[i] * a.c;
+      part = fmaf(q[i], km[i], part);
+    }
+    bias = group_sum<LPR>(part) * a.c;
+  }
+  // Codes of the new token (only wave 0 writes them), computed while the
+  // first rows are in flight.
+  CT kn_codes{}, vn_codes{};
+  float vs = 0.f, vmn = 0.f;
+  if (wave == 0) {
+    float kn[16], vn[16];
+    kn_raw.unpack(kn);
+    vn_raw.unpack(vn);
+    vmn = vn[0];
+    float vmx = vn[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      vmn = fminf(vmn, vn[i]);
+      vmx = fmaxf(vmx, vn[i]);
+    }
+    vmn = lane_group<LPR>(vmn, OpMin());
+    vmx = lane_group<LPR>(vmx, OpMax());
+    vs = grid_scale<BITS>(vmn, vmx);
+    uint32_t kc[16], vc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      kc[i] = quantize_code<BITS>(kn[i], ks[i], km[i]);
+      vc[i] = quantize_code<BITS>(vn[i], vs, vmn);
+    }
+    kn_codes = LC::pack(kc);
+    vn_codes = LC::pack(vc);
+  }
+  float sc_pf[PF];
+  int pos_pf[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int slot = tid + NT * i;
+    sc_pf[i] = 0.f;
+    pos_pf[i] = 0;
+    if (slot < nu) {
+      sc_pf[i] = a.score[hrow + slot];
+      pos_pf[i] = a.pos[hrow + slot];
+    }
+  }
+
+  // ---- stream this wave's rows -------------------------------------------------------
+  const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * RB + sub * CB;
+  const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * RB + sub * CB;
+  const float2* vg = reinterpret_cast<const float2*>(a.v_qparam) + hrow;
+  float m = kNegInf, l = 0.f, pm = 0.f;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const int units = (nu + RPU - 1) / RPU;
+  const int nb = (units + WAVES * UB - 1) / (WAVES * UB);  // batches per wave
+  auto row_of = [&](int b, int j) { return ((b * UB + j) * WAVES + wave) * RPU + grp; };
+  auto issue = [&](CT (&kb)[UB], CT (&vb)[UB], float2 (&gb)[UB], int b) {
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+      const int row = min(row_of(b, j), nu - 1);
+      kb[j] = LC::load(Kh + size_t(row) * RB);
+      vb[j] = LC::load(Vh + size_t(row) * RB);
+      gb[j] = vg[row];
+    }
+  };
+  auto compute = [&](const CT (&kb)[UB], const CT (&vb)[UB], const float2 (&gb)[UB], int b) {
+    float s[UB];
+    float bm = kNegInf;
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+      const int row = row_of(b, j);
+      float c[16];
+      LC::to_float(kb[j], c);
+      float x4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x4[i % 4] = fmaf(qs[i], c[i], x4[i % 4]);
+      const float x = group_sum<LPR>((x4[0] + x4[1]) + (x4[2] + x4[3])) + bias;
+      s[j] = row < nu ? x : kNegInf;
+      bm = fmaxf(bm, s[j]);
+      if (sub == 0 && row < nu) sm_logit[row] = s[j];
+    }
+    if (bm != kNegInf) {
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+      pm *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] *= alpha;
+#pragma unroll
+      for (int j = 0; j < UB; ++j) {
+        const float p = fast_exp2(s[j] - mn);
+        l += p;
+        pm = fmaf(p, gb[j].y, pm);
+        const float ps = p * gb[j].x;
+        float c[16];
+        LC::to_float(vb[j], c);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = fmaf(ps, c[i], acc[i]);
+      }
+      m = mn;
+    }
+  };
+  if (nu > 0) {
+    CT kA[UB], vA[UB], kB[UB], vB[UB];
+    float2 gA[UB], gB[UB];
+    issue(kA, vA, gA, 0);
+    for (int b = 0; b < nb; b += 2) {
+      issue(kB, vB, gB, b + 1);
+      compute(kA, vA, gA, b);
+      issue(kA, vA, gA, b + 2);
+      compute(kB, vB, gB, b + 1);
+    }
+  }
+
+  // ---- merge: lane groups inside the wave, then the waves through LDS -----------------
+  float qf[16], kn[16], vn[16];
+  q_raw.unpack(qf);
+  kn_raw.unpack(kn);
+  vn_raw.unpack(vn);
+  float sn = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sn = fmaf(qf[i], kn[i], sn);
+  const float s_new = group_sum<LPR>(sn) * a.c;  // the new token at full precision
+  // Every wave's reference includes s_new, so it is finite even for a wave
+  // that streamed no occupied row.
+  const float Mw = fmaxf(across_groups<LPR>(m, OpMax()), s_new);
+  const float w = fast_exp2(m - Mw);
+  const float lw = across_groups<LPR>(l * w, OpAdd());
+  const float pmw = across_groups<LPR>(pm * w, OpAdd());
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = across_groups<LPR>(acc[i] * w, OpAdd());
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 4)
+      *reinterpret_cast<float4*>(&sm_acc[wave][c0 + i]) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+  }
+  if (lane == 0) {
+    sm_m[wave] = Mw;
+    sm_l[wave] = lw;
+    sm_pm[wave] = pmw;
+  }
+  __syncthreads();
+  float M = sm_m[0];
+#pragma unroll
+  for (int v = 1; v < WAVES; ++v) M = fmaxf(M, sm_m[v]);
+  float f[WAVES];
+  float Z = 0.f, PM = 0.f;
+#pragma unroll
+  for (int v = 0; v < WAVES; ++v) {
+    f[v] = fast_exp2(sm_m[v] - M);
+    Z = fmaf(sm_l[v], f[v], Z);
+    PM = fmaf(sm_pm[v], f[v], PM);
+  }
+  const float w_new = fast_exp2(s_new - M);
+  const float invZ = 1.0f / (Z + w_new);
+  if (wave == 0 && grp == 0) {
+    float* op = a.out + size_t(head) * D + c0;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = 0.f;
+#pragma unroll
+        for (int v = 0; v < WAVES; ++v) x = fmaf(sm_acc[v][c0 + i + e], f[v], x);
+        o[e] = (x + PM + w_new * vn[i + e]) * invZ;
+      }
+      *reinterpret_cast<float4*>(op + i) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+
+  // ---- accumulate scores, pick the victim ----------------------------------------------
+  const float p_new = w_new * invZ;
+  const bool full = nu == a.k;
+  const int lim = a.t - a.k_recent;
+  float* sc_g = a.score + hrow;
+  int32_t* pos_g = a.pos + hrow;
+  uint64_t best = ~0ull;
+  int best_slot = -1, best_pos = -1;
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int slot = tid + NT * i;
+    if (slot < nu) {
+      const float sc = sc_pf[i] + fast_exp2(sm_logit[slot] - M) * invZ;
+      sc_g[slot] = sc;
+      if (full && pos_pf[i] <= lim) {
+        const uint64_t key = evict_key(sc, pos_pf[i], a.t, a.policy);
+        if (key < best) {
+          best = key;
+          best_slot = slot;
+          best_pos = pos_pf[i];
+        }
+      }
+    }
+  }
+  for (int slot = tid + NT * PF; slot < nu; slot += NT) {
+    const float sc = sc_g[slot] + fast_exp2(sm_logit[slot] - M) * invZ;
+    const int ps = pos_g[slot];
+    sc_g[slot] = sc;
+    if (full && ps <= lim) {
+      const uint64_t key = evict_key(sc, ps, a.t, a.policy);
+      if (key < best) {
+        best = key;
+        best_slot = slot;
+        best_pos = ps;
+      }
+    }
+  }
+  // Without a recent window the new token competes too (slot k = "itself").
+  if (full && a.k_recent == 0 && tid == 0) {
+    const uint64_t key = evict_key(p_new, a.t, a.t, a.policy);
+    if (key < best) {
+      best = key;
+      best_slot = a.k;
+      best_pos = a.t;
+    }
+  }
+  int victim = nu;
+  int evicted = -1;
+  if (full) {
+    const uint64_t gmin = wave_min_u64(best);
+    // Keys are unique (positions are), so at most one lane holds the minimum.
+    const uint64_t owners = __ballot(best == gmin && gmin != ~0ull);
+    if (lane == 0) {
+      sm_key[wave] = gmin;
+      sm_slot[wave] = -1;
+      sm_epos[wave] = -2;
+    }
+    if (owners) {
+      const int owner = __ffsll((unsigned long long)owners) - 1;
+      const int vslot = __builtin_amdgcn_readlane(best_slot, owner);
+      const int vpos = __builtin_amdgcn_readlane(best_pos, owner);
+      if (lane == 0) {
+        sm_slot[wave] = vslot;
+        sm_epos[wave] = vpos;
+      }
+    }
+  }
+  __syncthreads();
+  if (full) {
+    uint64_t k_best = sm_key[0];
+    int vb = 0;
+#pragma unroll
+    for (int v = 1; v < WAVES; ++v)
+      if (sm_key[v] < k_best) {
+        k_best = sm_key[v];
+        vb = v;
+      }
+    // A full cache always has an eligible candidate; if the caller's state
+    // broke that invariant nothing is written and -2 is reported.
+    victim = k_best == ~0ull ? -1 : sm_slot[vb];
+    evicted = k_best == ~0ull ? -2 : sm_epos[vb];
+  }
+
+  // ---- insert the new token, quantised ---------------------------------------------------
+  if (victim >= 0 && victim < a.k) {
+    if (tid == victim % NT) {
+      sc_g[victim] = p_new;
+      pos_g[victim] = a.t;
+    }
+    if (wave == 0 && grp == 0) {
+      LC::store(static_cast<uint8_t*>(a.K_w) + (hrow + victim) * RB + sub * CB, kn_codes);
+      LC::store(static_cast<uint8_t*>(a.V_w) + (hrow + victim) * RB + sub * CB, vn_codes);
+      if (sub == 0) reinterpret_cast<float2*>(a.v_qparam)[hrow + victim] = make_float2(vs, vmn);
+    }
+  }
+  if (tid == 0) a.evicted[head] = evicted;
+}
+
 template <int DT, int D, int BITS>
 hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
   // K and V codes per batch: 2 KiB at 8 and 4 bits (2 or 4 wave-loads), 1 KiB
   // at 2 bits (4 wave-loads; 8 would spill registers).
   constexpr int UB = BITS == 8 ? 2 : 4, PF = 4, MINW = 2;
   const int resident = cu_count() * 4 * MINW;
-  const int grid = G < resident ? G : resident;
   const size_t shmem = size_t(a.k) * sizeof(float);
-  hipLaunchKernelGGL((decode_quant_kernel<DT, D, BITS, UB, PF>), dim3(grid), dim3(64), shmem, s, a, G);
+  if (G >= resident / 2) {
+    const int grid = G < resident ? G : resident;
+    hipLaunchKernelGGL((decode_quant_kernel<DT, D, BITS, UB, PF>), dim3(grid), dim3(64), shmem, s, a, G);
+  } else {
+    // Few heads: an 8-wave workgroup per head, as for caches of rows.
+    constexpr int WAVES = 8;
+    hipLaunchKernelGGL((decode_quant_wg_kernel<DT, D, BITS, WAVES, UB, PF>), dim3(G), dim3(WAVES * 64), shmem, s,
+                       a);
+  }
   return hipGetLastError();
 }
 
