@@ -24,6 +24,8 @@
 // recent window (H2O §A "Pseudocode", "System Details") and copies the K/V
 // rows into the cache slots.
 
+#include <type_traits>
+
 #include "../../include/h2o.h"
 #include "h2o_device.h"
 #include "launch.h"
@@ -39,6 +41,10 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int grid) {
   const int per = grid >> 3;  // grid is padded to a multiple of 8
   return (bid & 7) * per + (bid >> 3);
 }
+
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data
+// format, no swizzle): untyped loads, range-checked against the record count.
+constexpr int kBufferWord3 = 0x00020000;
 
 template <int DT> struct MfmaOp;
 template <> struct MfmaOp<DT_BF16> {
@@ -89,12 +95,17 @@ struct Tile64 {
   }
   __device__ __forceinline__ static int my_chunk() { return (threadIdx.x & 63) % CH; }
 
-  // Fetch rows [r0, r0 + 64) (clamped to n - 1) of `src` into registers.
-  __device__ __forceinline__ static void fetch(uint4 (&r)[CPT], const char* src, int r0, int n) {
+  // A head's n rows as a buffer resource: loads past row n - 1 return zeros
+  // (range-checked by the load itself), so tiles need no clamping.
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rows(const char* head_base, int n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(head_base), 0, n * ROW, kBufferWord3);
+  }
+  // Fetch rows [r0, r0 + 64) of `src` into registers (zeros past the end).
+  __device__ __forceinline__ static void fetch(uint4 (&r)[CPT], __amdgpu_buffer_rsrc_t src, int r0) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int row = min(r0 + my_row(i), n - 1);
-      r[i] = ld16(src + size_t(row) * ROW + my_chunk() * 16);
+      const uint32_t off = uint32_t((r0 + my_row(i)) * ROW + my_chunk() * 16);
+      r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(src, off, 0, 0));
     }
   }
   __device__ __forceinline__ static void store(char* lds, const uint4 (&r)[CPT]) {
@@ -120,6 +131,19 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // per wave); keys streamed in 64-row LDS tiles. The transposed tile (keys x
 // queries) gives each lane one query column, so the row statistics are
 // in-lane until the final merge of the two lane halves.
+//
+// Each lane keeps a reference r (log2 domain) and l = sum 2^(c*s - r). r is
+// the maximum of the first tile the lane sees, and stays fixed while a
+// tile's partial sum stays below 2^64 (every term below 2^58 of the
+// reference): then a score costs one FMA, one exp2 and one add, with no
+// max. A tile whose sum overflows that bound, or the first tile, takes the
+// exact path instead: tile maximum, rescale of l, new reference. The sum is
+// the same up to fp32 rounding whatever the reference, since fp32 keeps its
+// relative precision over the whole range involved.
+//
+// Key tiles below the workgroup's first query are visible to all of its
+// queries and run without the causal mask; only the last NW tiles (the
+// diagonal) test positions.
 template <int DT, int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
   using T = Tile64<DT, D, NW>;
@@ -136,6 +160,7 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
   const int q0 = wg_q0 + wave * 64;
   const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
   const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
+  const auto Kr = T::rows(Kh, n);
   const float c = a.c;
 
   uint4 qf[2][T::KS];
@@ -146,17 +171,51 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
     for (int ks = 0; ks < T::KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
   }
   wait_vmem_all();
-  float m[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+  float ref[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
   const int ntiles = min(wg_q0 + QBLK - 1, n - 1) / 64 + 1;
+  const int nfull = min(wg_q0 / 64, ntiles);  // tiles with every key <= the workgroup's first query
   uint4 nx[T::CPT];
-  T::fetch(nx, Kh, 0, n);
+  T::fetch(nx, Kr, 0);
   T::store(lds[0], nx);
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    if (kt + 1 < ntiles) T::fetch(nx, Kh, (kt + 1) * 64, n);
+
+  auto accumulate = [&](const f32x16 (&acc)[2][2], int cb) {
+    const float nr = -ref[cb];
+    float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      t0 += fast_exp2(fmaf(acc[0][cb][j], c, nr));
+      t1 += fast_exp2(fmaf(acc[1][cb][j], c, nr));
+    }
+    const float t = t0 + t1;
+    if (t <= 0x1p64f) {
+      l[cb] += t;
+    } else {  // first tile (reference -inf), or a score far above the reference; also NaN
+      float tm = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][cb][j], acc[0][cb][j + 1]);
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
+      const float rn = fmaxf(ref[cb], tm * c);
+      if (rn != kNegInf) {
+        float u0 = 0.f, u1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          u0 += fast_exp2(fmaf(acc[0][cb][j], c, -rn));
+          u1 += fast_exp2(fmaf(acc[1][cb][j], c, -rn));
+        }
+        l[cb] = fmaf(l[cb], fast_exp2(ref[cb] - rn), u0 + u1);
+        ref[cb] = rn;
+      }
+    }
+  };
+
+  auto step = [&](int kt, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    if (kt + 1 < ntiles) T::fetch(nx, Kr, (kt + 1) * 64);
     const char* buf = lds[kt & 1];
     const int key0 = kt * 64;
-    if (key0 <= min(q0 + 63, n - 1)) {  // some key of the tile is visible to this wave
+    if (!MASKED || key0 <= min(q0 + 63, n - 1)) {  // some key of the tile is visible to this wave
       f32x16 acc[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -173,44 +232,32 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
       // acc[kb][cb][j] = s(query q0 + 32cb + lane%32, key key0 + 32kb + mfma_row(j))
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const int qi = q0 + cb * 32 + (lane & 31);
-        if (key0 + 63 > q0 + cb * 32) {  // tile reaches past some query of this block: mask
+        if constexpr (MASKED) {
+          const int qi = q0 + cb * 32 + (lane & 31);
+          if (key0 + 63 > q0 + cb * 32) {  // tile reaches past some query of this block
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][cb][j] = kNegInf;
-        }
-        float tm = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][cb][j], acc[0][cb][j + 1]);
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
-        const float mn = fmaxf(m[cb], tm);
-        if (mn != kNegInf) {
-          const float mnc = mn * c;
-          float t0 = 0.f, t1 = 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            t0 += fast_exp2(fmaf(acc[0][cb][j], c, -mnc));
-            t1 += fast_exp2(fmaf(acc[1][cb][j], c, -mnc));
+              for (int j = 0; j < 16; ++j)
+                if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][cb][j] = kNegInf;
           }
-          l[cb] = fmaf(l[cb], fast_exp2((m[cb] - mn) * c), t0 + t1);
-          m[cb] = mn;
         }
+        accumulate(acc, cb);
       }
     }
     if (kt + 1 < ntiles) T::store(lds[(kt + 1) & 1], nx);
     __syncthreads();
-  }
+  };
+  for (int kt = 0; kt < nfull; ++kt) step(kt, std::false_type{});
+  for (int kt = nfull; kt < ntiles; ++kt) step(kt, std::true_type{});
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const float mo = __shfl_xor(m[cb], 32);
+    const float ro = __shfl_xor(ref[cb], 32);
     const float lo = __shfl_xor(l[cb], 32);
-    const float M = fmaxf(m[cb], mo);
-    const float Lsum = l[cb] * fast_exp2((m[cb] - M) * c) + lo * fast_exp2((mo - M) * c);
+    const float M = fmaxf(ref[cb], ro);
+    const float Lsum = l[cb] * fast_exp2(ref[cb] - M) + lo * fast_exp2(ro - M);
     const int qi = q0 + cb * 32 + (lane & 31);
-    if (lh == 0 && qi < n) a.lse2[size_t(head) * ld_lse + qi] = M * c + fast_log2(Lsum);
+    if (lh == 0 && qi < n) a.lse2[size_t(head) * ld_lse + qi] = M + fast_log2(Lsum);
   }
 }
 
@@ -301,6 +348,8 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
   const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
   const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
   const char* Vh = static_cast<const char*>(a.V) + size_t(head) * n * T::ROW;
+  const auto Kr = T::rows(Kh, n);
+  const auto Vr = T::rows(Vh, n);
   const float c = a.c;
 
   uint4 qf[T::KS];
@@ -316,16 +365,16 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
   float m = kNegInf, l = 0.f;
   const int ntiles = min(wg_q0 + 255, n - 1) / 64 + 1;
   uint4 nk[T::CPT], nv[T::CPT];
-  T::fetch(nk, Kh, 0, n);
-  T::fetch(nv, Vh, 0, n);
+  T::fetch(nk, Kr, 0);
+  T::fetch(nv, Vr, 0);
   T::store(lds_k[0], nk);
   VT::store(lds_v[0], nv);
   __syncthreads();
   const int qi = q0 + (lane & 31);
   for (int kt = 0; kt < ntiles; ++kt) {
     if (kt + 1 < ntiles) {
-      T::fetch(nk, Kh, (kt + 1) * 64, n);
-      T::fetch(nv, Vh, (kt + 1) * 64, n);
+      T::fetch(nk, Kr, (kt + 1) * 64);
+      T::fetch(nv, Vr, (kt + 1) * 64);
     }
     const char* kbuf = lds_k[kt & 1];
     const char* vbuf = lds_v[kt & 1];
@@ -428,6 +477,7 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
   const int k0 = wg_k0 + wave * 64;
   const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
   const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
+  const auto Qr = T::rows(Qh, n);
   const float* lse = a.lse2 + size_t(head) * ld_lse;
   const float c = a.c;
 
@@ -447,7 +497,7 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
   // Rows past the prompt get lse = +inf, so their terms are exp2(-inf) = 0
   // without a per-element test.
   auto fetch = [&](int qt) {
-    T::fetch(nx, Qh, qt * 64, n);
+    T::fetch(nx, Qr, qt * 64);
     if (threadIdx.x < 64) {
       const int q = qt * 64 + threadIdx.x;
       nl = q < n ? lse[q] : __builtin_huge_valf();
@@ -460,11 +510,12 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
   fetch(t0);
   store(0);
   __syncthreads();
-  for (int qt = t0; qt < ntiles; ++qt) {
+  auto step = [&](int qt, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cur = (qt - t0) & 1;
     if (qt + 1 < ntiles) fetch(qt + 1);
     const int qrow0 = qt * 64;
-    if (qrow0 + 63 >= k0 && k0 < n) {  // some query of the tile sees a key of this wave
+    if (!MASKED || (qrow0 + 63 >= k0 && k0 < n)) {  // some query of the tile sees a key of this wave
       const char* buf = lds[cur];
       f32x16 acc[2][2];
 #pragma unroll
@@ -493,13 +544,15 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
         }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int kj = k0 + kb * 32 + (lane & 31);
-        if (qrow0 < k0 + kb * 32 + 31) {  // diagonal tile: queries before the key see nothing
+        if constexpr (MASKED) {
+          const int kj = k0 + kb * 32 + (lane & 31);
+          if (qrow0 < k0 + kb * 32 + 31) {  // diagonal tile: queries before the key see nothing
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
+            for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-              acc[qb][kb][j] = qrow0 + qb * 32 + mfma_row(j, lane) < kj ? kNegInf : acc[qb][kb][j];
+              for (int j = 0; j < 16; ++j)
+                acc[qb][kb][j] = qrow0 + qb * 32 + mfma_row(j, lane) < kj ? kNegInf : acc[qb][kb][j];
+          }
         }
         float t = 0.f, t2 = 0.f;
 #pragma unroll
@@ -516,7 +569,12 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
     }
     if (qt + 1 < ntiles) store(cur ^ 1);
     __syncthreads();
-  }
+  };
+  // Query tiles [t0, t0 + NW) hold the diagonal of some wave of the
+  // workgroup; every later tile is visible to all of its keys.
+  const int tdiag = min(t0 + NW, ntiles);
+  for (int qt = t0; qt < tdiag; ++qt) step(qt, std::true_type{});
+  for (int qt = tdiag; qt < ntiles; ++qt) step(qt, std::false_type{});
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const float mine = sum[kb] - comp[kb];
