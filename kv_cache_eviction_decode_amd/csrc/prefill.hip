@@ -216,6 +216,10 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
     const char* buf = lds[kt & 1];
     const int key0 = kt * 64;
     if (!MASKED || key0 <= min(q0 + 63, n - 1)) {  // some key of the tile is visible to this wave
+      // The MFMA chain issues at raised priority, so that while this wave
+      // feeds the matrix unit the other wave of the SIMD fills the gaps with
+      // its exp/sum work instead of delaying the chain (long prompts: 5%).
+      __builtin_amdgcn_s_setprio(1);
       f32x16 acc[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -229,6 +233,7 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
           for (int ks = 0; ks < T::KS; ++ks) acc[kb][cb] = MfmaOp<DT>::run(af[ks], qf[cb][ks], acc[kb][cb]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // acc[kb][cb][j] = s(query q0 + 32cb + lane%32, key key0 + 32kb + mfma_row(j))
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
@@ -371,7 +376,10 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
   VT::store(lds_v[0], nv);
   __syncthreads();
   const int qi = q0 + (lane & 31);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // Key tiles below the workgroup's first query need no causal mask.
+  const int nfull = min(wg_q0 / 64, ntiles);
+  auto step = [&](int kt, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     if (kt + 1 < ntiles) {
       T::fetch(nk, Kr, (kt + 1) * 64);
       T::fetch(nv, Vr, (kt + 1) * 64);
@@ -379,7 +387,7 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
     const char* kbuf = lds_k[kt & 1];
     const char* vbuf = lds_v[kt & 1];
     const int key0 = kt * 64;
-    if (key0 <= min(q0 + 31, n - 1)) {  // every query of this wave sees key0
+    if (!MASKED || key0 <= min(q0 + 31, n - 1)) {  // every query of this wave sees key0
       f32x16 acc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -388,12 +396,14 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
         for (int ks = 0; ks < T::KS; ++ks) acc[kb] = MfmaOp<DT>::run(T::frag(kbuf, kb, ks, lane), qf[ks], acc[kb]);
       }
       // acc[kb][j] = s(query qi, key key0 + 32kb + mfma_row(j))
-      if (key0 + 63 > q0) {
+      if constexpr (MASKED) {
+        if (key0 + 63 > q0) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][j] = kNegInf;
+            for (int j = 0; j < 16; ++j)
+              if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][j] = kNegInf;
+        }
       }
       float tm = kNegInf;
 #pragma unroll
@@ -437,7 +447,9 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
       VT::store(lds_v[(kt + 1) & 1], nv);
     }
     __syncthreads();
-  }
+  };
+  for (int kt = 0; kt < nfull; ++kt) step(kt, std::false_type{});
+  for (int kt = nfull; kt < ntiles; ++kt) step(kt, std::true_type{});
   const float lt = l + __shfl_xor(l, 32);  // both halves share the reference maximum
   if (qi < n) {
     const float lse2 = m * c + fast_log2(lt);
@@ -517,6 +529,7 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
     const int qrow0 = qt * 64;
     if (!MASKED || (qrow0 + 63 >= k0 && k0 < n)) {  // some query of the tile sees a key of this wave
       const char* buf = lds[cur];
+      __builtin_amdgcn_s_setprio(1);  // as in rowlse_lds (neutral here, kept for symmetry)
       f32x16 acc[2][2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -530,6 +543,7 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
           for (int ks = 0; ks < T::KS; ++ks) acc[qb][kb] = MfmaOp<DT>::run(af[ks], kf[kb][ks], acc[qb][kb]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // acc[qb][kb][j] = s(query qrow0 + 32qb + mfma_row(j), key k0 + 32kb + lane%32)
       float lq[2][16];
 #pragma unroll
