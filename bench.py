@@ -65,6 +65,9 @@ def parse_args():
                         "(h2o_cache_init_quant)")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-oracle sample (0: enough for about 15 s of oracle work)")
+    p.add_argument("--fullcache", action="store_true",
+                   help="also time a no-eviction decode attention over the full final length (prompt + decode "
+                        "steps) on the same inputs (always on for large_batch_f16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-single-layer", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -88,6 +91,12 @@ def decode_bytes_per_head(n_used: int, d: int, e: int) -> int:
     row (fp32), the new K and V rows, the new slot's pos, the evicted position.
     """
     return 2 * n_used * d * e + 12 * n_used + 5 * d * e + 4 * d + 8
+
+
+def fullcache_bytes_per_head(length: int, d: int, e: int) -> int:
+    """Algorithmic HBM bytes of one no-eviction decode attention for one (batch, head):
+    K and V rows of every cached position, the query, the fp32 output row."""
+    return 2 * length * d * e + d * e + 4 * d
 
 
 def decode_bytes_per_head_quant(n_used: int, d: int, e: int, bits: int) -> int:
@@ -311,6 +320,41 @@ def main():
                   "note": f"one cache decoded alone: its {bytes_per_launch / 1e6:.0f} MB per step can be partly "
                           "re-read from the 256 MB Infinity Cache"}
 
+    fullcache = None
+    if args.fullcache or wl.name == "large_batch_f16":
+        # The comparator of the large-batch workload: the same step without
+        # eviction, i.e. plain decode attention over every position of the
+        # final length, with the same prompt and decode keys/values.
+        from kv_cache_eviction_decode_amd import h2o_fullcache_decode
+        Lf = n + T
+        Kc = torch.cat([K, ks.permute(1, 2, 0, 3)], dim=2).contiguous()
+        Vc = torch.cat([V, vs.permute(1, 2, 0, 3)], dim=2).contiguous()
+        fout = torch.empty(B, H, d, dtype=torch.float32, device=dev)
+        reps = 20
+        for _ in range(3):
+            h2o_fullcache_decode(qs[T - 1], Kc, Vc, fout, wl.scale, stream)
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(reps):
+            h2o_fullcache_decode(qs[T - 1], Kc, Vc, fout, wl.scale, stream)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        f_s = f0.elapsed_time(f1) / 1e3 / reps
+        f_bytes = G * fullcache_bytes_per_head(Lf, d, e)
+        h2o_full_bytes = G * decode_bytes_per_head(k, d, e)
+        fullcache = {"kernel": "h2o decode_wave_kernel, unscored mode (no scores, no eviction)",
+                     "length": Lf, "us_per_launch": f_s * 1e6, "head_steps_per_s": G / f_s,
+                     "GBps": f_bytes / f_s / 1e9, "hbm_frac": f_bytes / f_s / 1e9 / HBM_PEAK_GBS,
+                     "bytes_per_launch": f_bytes,
+                     "h2o_bytes_per_launch_full_cache": h2o_full_bytes,
+                     "bytes_ratio_fullcache_over_h2o": f_bytes / h2o_full_bytes,
+                     "h2o_avg_launch_us": avg_launch_s * 1e6,
+                     "time_ratio_fullcache_over_h2o": f_s / avg_launch_s,
+                     "note": f"{reps} launches over a {Lf}-position cache after 3 warm-up launches, query of the "
+                             "last decode step; H2O bytes are those of a full k-slot step"}
+        del Kc, Vc
+
     result = {
         "metric": METRIC,
         "value": value,
@@ -343,6 +387,7 @@ def main():
                              if attn else "rowlse + colsum + select/gather + cache clear, 2 causal QK^T passes")},
         "wall_s_timed": wall_s,
         "single_layer": single,
+        "fullcache": fullcache,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
