@@ -29,6 +29,10 @@ SMALL = [
     ("sink_f16_d128", 1, 2, 128, "f16", 2048, 205, 205, 16, 1.5, 4.0),
     ("f32_d64_odd_k", 2, 2, 64, "f32", 200, 7, 6, 30, 1.2, 0.0),
     ("bf16_long_tail", 1, 1, 128, "bf16", 1500, 100, 1, 24, 1.2, 0.0),
+    # prompts over 2048 tokens take 4-wave workgroups; a ragged last block
+    # leaves whole waves past the prompt (2100) or one wave partly inside (2500)
+    ("ragged_4wave_bf16", 1, 2, 128, "bf16", 2100, 64, 64, 8, 1.5, 0.0),
+    ("ragged_4wave_f16_d64", 1, 1, 64, "f16", 2500, 30, 31, 6, 1.2, 0.0),
 ]
 
 
