@@ -33,9 +33,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
 METRIC = "H2O decode head-steps/sec + achieved HBM GB/s (% of MI355X peak)"
 DECODE_SOURCES = {"fused": ["decode.hip", "h2o_device.h", "launch.h"],
                   "split": ["decode_split.hip", "h2o_device.h", "launch.h"],
-                  "u8": ["decode_quant.hip", "h2o_device.h", "launch.h"],
-                  "u4": ["decode_quant.hip", "h2o_device.h", "launch.h"],
-                  "u2": ["decode_quant.hip", "h2o_device.h", "launch.h"]}
+                  "u8": ["decode_quant.hip", "lane_codes.h", "h2o_device.h", "launch.h"],
+                  "u4": ["decode_quant.hip", "lane_codes.h", "h2o_device.h", "launch.h"],
+                  "u2": ["decode_quant.hip", "lane_codes.h", "h2o_device.h", "launch.h"]}
 QUANT_BITS = {"u8": 8, "u4": 4, "u2": 2}
 
 

@@ -23,6 +23,7 @@
 // The new token's key and value are quantised on insert.
 
 #include "h2o_device.h"
+#include "lane_codes.h"
 #include "launch.h"
 
 namespace h2o {
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G
       float part = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        qs[i] = q[i] * ks[i] * a.c;
+        qs[i] = q[i] * ks[i] * a.c * LC::inv_weight(i);  // codes come weighted
         part = fmaf(q[i], km[i], part);
       }
       bias = group_sum<LPR>(part) * a.c;
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G
     const float lw = across_groups<LPR>(l * w, OpAdd());
     const float pmw = across_groups<LPR>(pm * w, OpAdd());
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = across_groups<LPR>(acc[i] * w, OpAdd());
+    for (int i = 0; i < 16; ++i) acc[i] = across_groups<LPR>(acc[i] * (w * LC::inv_weight(i)), OpAdd());
     const float w_new = fast_exp2(s_new - M);
     const float invZ = 1.0f / (lw + w_new);
     if (grp == 0) {
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void decode_quant_wg_kernel(DecodeAr
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      qs[i] = q[i] * ks[i] * a.c;
+      qs[i] = q[i] * ks[i] * a.c * LC::inv_weight(i);  // codes come weighted
       part = fmaf(q[i], km[i], part);
     }
     bias = group_sum<LPR>(part) * a.c;
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void decode_quant_wg_kernel(DecodeAr
   const float lw = across_groups<LPR>(l * w, OpAdd());
   const float pmw = across_groups<LPR>(pm * w, OpAdd());
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = across_groups<LPR>(acc[i] * w, OpAdd());
+  for (int i = 0; i < 16; ++i) acc[i] = across_groups<LPR>(acc[i] * (w * LC::inv_weight(i)), OpAdd());
   if (grp == 0) {
 #pragma unroll
     for (int i = 0; i < 16; i += 4)

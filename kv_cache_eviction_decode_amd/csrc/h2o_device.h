@@ -222,71 +222,6 @@ template <int BITS> __device__ __forceinline__ uint32_t quantize_code(float x, f
 // 16 consecutive channels of a code row held by one lane: 2 * BITS bytes,
 // channel i at bit offset BITS * i of the lane's little-endian bytes. Loads
 // are non-temporal (rows are streamed once per step).
-template <int BITS> struct LaneCodes;
-template <> struct LaneCodes<8> {
-  using T = uint4;
-  __device__ __forceinline__ static T load(const uint8_t* p) { return ldnt16(p); }
-  __device__ __forceinline__ static void store(uint8_t* p, T v) { *reinterpret_cast<uint4*>(p) = v; }
-  __device__ __forceinline__ static void to_float(T w, float (&c)[16]) {
-    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) c[4 * i + b] = float((v[i] >> (8 * b)) & 0xFFu);
-  }
-  __device__ __forceinline__ static T pack(const uint32_t (&c)[16]) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = c[4 * i] | c[4 * i + 1] << 8 | c[4 * i + 2] << 16 | c[4 * i + 3] << 24;
-    return make_uint4(w[0], w[1], w[2], w[3]);
-  }
-};
-template <> struct LaneCodes<4> {
-  using T = uint2;
-  __device__ __forceinline__ static T load(const uint8_t* p) { return ldnt8(p); }
-  __device__ __forceinline__ static void store(uint8_t* p, T v) { *reinterpret_cast<uint2*>(p) = v; }
-  // Word i holds channels 8i..8i+7; masking the low and the high nibbles
-  // leaves the even and the odd channels one per byte.
-  __device__ __forceinline__ static void to_float(T w, float (&c)[16]) {
-    const uint32_t v[2] = {w.x, w.y};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t lo = v[i] & 0x0F0F0F0Fu, hi = (v[i] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        c[8 * i + 2 * b] = float((lo >> (8 * b)) & 0xFFu);
-        c[8 * i + 2 * b + 1] = float((hi >> (8 * b)) & 0xFFu);
-      }
-    }
-  }
-  __device__ __forceinline__ static T pack(const uint32_t (&c)[16]) {
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w[i / 8] |= c[i] << (4 * (i % 8));
-    return make_uint2(w[0], w[1]);
-  }
-};
-template <> struct LaneCodes<2> {
-  using T = uint32_t;
-  __device__ __forceinline__ static T load(const uint8_t* p) { return ldnt4(p); }
-  __device__ __forceinline__ static void store(uint8_t* p, T v) { *reinterpret_cast<uint32_t*>(p) = v; }
-  // Byte b holds channels 4b..4b+3; the j-th crumb of every byte is channel 4b + j.
-  __device__ __forceinline__ static void to_float(T w, float (&c)[16]) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t part = (w >> (2 * j)) & 0x03030303u;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) c[4 * b + j] = float((part >> (8 * b)) & 0xFFu);
-    }
-  }
-  __device__ __forceinline__ static T pack(const uint32_t (&c)[16]) {
-    uint32_t w = 0u;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w |= c[i] << (2 * i);
-    return w;
-  }
-};
-
 template <int CTRL> __device__ __forceinline__ uint64_t dpp64(uint64_t x) {
   const uint32_t lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(x)), CTRL, 0xF, 0xF, false);
   const uint32_t hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(x >> 32)), CTRL, 0xF, 0xF, false);
