@@ -44,6 +44,13 @@ template <int DT> struct Raw16 {
   }
 };
 
+// The softmax reference of a lane group moves only when a batch's maximum
+// exceeds it by more than this (base 2; probabilities stay below 2^8), and
+// the accumulators are rescaled only when some lane of the wave moved it,
+// which after a head's first batches is rare. Numerator and normaliser share
+// the reference, so the result is the same.
+constexpr float kLazyRef = 8.0f;
+
 // One wave per head.
 //   BITS: code width; UB: wave-loads of codes (K and V, 128 * BITS bytes each)
 //   per batch; PF: score/pos entries per lane prefetched with the head's inputs.
@@ -173,15 +180,19 @@ __global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G
         if (sub == 0 && row < nu) sm_logit[row] = s[j];
       }
       if (bm != kNegInf) {
-        const float mn = fmaxf(m, bm);
-        const float alpha = fast_exp2(m - mn);
-        l *= alpha;
-        pm *= alpha;
+        const bool raise = bm > m + kLazyRef;  // always on a group's first rows (m = -inf)
+        if (__ballot(raise)) {
+          const float mn = raise ? bm : m;
+          const float alpha = fast_exp2(m - mn);
+          l *= alpha;
+          pm *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] *= alpha;
+          for (int i = 0; i < 16; ++i) acc[i] *= alpha;
+          m = mn;
+        }
 #pragma unroll
         for (int j = 0; j < UB; ++j) {
-          const float p = fast_exp2(s[j] - mn);
+          const float p = fast_exp2(s[j] - m);
           l += p;
           pm = fmaf(p, gb[j].y, pm);
           const float ps = p * gb[j].x;
@@ -190,7 +201,6 @@ __global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[i] = fmaf(ps, c[i], acc[i]);
         }
-        m = mn;
       }
     };
     if (nb > 0) {
@@ -444,15 +454,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void decode_quant_wg_kernel(DecodeAr
       if (sub == 0 && row < nu) sm_logit[row] = s[j];
     }
     if (bm != kNegInf) {
-      const float mn = fmaxf(m, bm);
-      const float alpha = fast_exp2(m - mn);
-      l *= alpha;
-      pm *= alpha;
+      const bool raise = bm > m + kLazyRef;  // always on a group's first rows (m = -inf)
+      if (__ballot(raise)) {
+        const float mn = raise ? bm : m;
+        const float alpha = fast_exp2(m - mn);
+        l *= alpha;
+        pm *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] *= alpha;
+        for (int i = 0; i < 16; ++i) acc[i] *= alpha;
+        m = mn;
+      }
 #pragma unroll
       for (int j = 0; j < UB; ++j) {
-        const float p = fast_exp2(s[j] - mn);
+        const float p = fast_exp2(s[j] - m);
         l += p;
         pm = fmaf(p, gb[j].y, pm);
         const float ps = p * gb[j].x;
@@ -461,7 +475,6 @@ __global__ __launch_bounds__(WAVES * 64, 2) void decode_quant_wg_kernel(DecodeAr
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = fmaf(ps, c[i], acc[i]);
       }
-      m = mn;
     }
   };
   if (nu > 0) {
