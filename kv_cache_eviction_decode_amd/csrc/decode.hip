@@ -516,9 +516,15 @@ hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
   if (G >= resident / 2) {
     // 4 wave-loads per batch (two batches in flight): 2% faster than 8 at the
     // OPT-6.7B, OPT-30B and large-batch shapes.
-    constexpr int UB = 4, PF = 4;
+    // Score/pos entries prefetched with the head's inputs: 4 per lane covers
+    // 256 slots; larger caches take 8, so that the epilogue loads nothing
+    // from HBM up to 512 slots (OPT-30B shape, 410 slots: 62.0 -> 61.4 us).
+    constexpr int UB = 4;
     const int grid = G < resident ? G : resident;
-    hipLaunchKernelGGL((decode_wave_kernel<DT, D, UB, PF, WMINW, SCORED>), dim3(grid), dim3(64), shmem, s, a, G);
+    if (a.k > 256)
+      hipLaunchKernelGGL((decode_wave_kernel<DT, D, UB, 8, WMINW, SCORED>), dim3(grid), dim3(64), shmem, s, a, G);
+    else
+      hipLaunchKernelGGL((decode_wave_kernel<DT, D, UB, 4, WMINW, SCORED>), dim3(grid), dim3(64), shmem, s, a, G);
   } else {
     // Few heads: spread each head over an 8-wave workgroup instead (two
     // waves per SIMD; against 4 waves: 32 heads x 2048 slots 33.5 -> 23.8 us,

@@ -97,6 +97,17 @@ def test_max_slots(gpu):
     log(f"[parity] max_slots: {rep}")
 
 
+def test_wave_kernel_beyond_prefetch(gpu):
+    """1024 heads (the one-wave-per-head kernel) with 640 slots: scores and
+    positions past the 512 prefetched per head are read in the epilogue."""
+    wl = Workload("wave_640", 32, 32, 128, "bf16", 900, 320, 320, 12, 1.5, 0.0, 77)
+    run = ParityRun(wl, wl.steps, sample=sample_heads(wl, 12))
+    run.prefill()
+    rep = run.decode()
+    log(f"[parity] wave kernel, 640 slots: {rep}")
+    assert rep.steps == wl.steps
+
+
 FULL = [("opt6.7b_layer", 512, 32), ("opt30b_layer", 64, 16),
         ("long_context", 24, 4), ("large_batch_f16", 48, 16)]
 
