@@ -320,6 +320,22 @@ def main():
                   "note": f"one cache decoded alone: its {bytes_per_launch / 1e6:.0f} MB per step can be partly "
                           "re-read from the 256 MB Infinity Cache"}
 
+    # Secondary denominator: what a plain device-to-device copy of 1 GiB
+    # moves per second on this GPU (bytes read + bytes written).
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    for _ in range(2):
+        cdst.copy_(csrc)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        cdst.copy_(csrc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del csrc, cdst
+
     fullcache = None
     if args.fullcache or wl.name == "large_batch_f16":
         # The comparator of the large-batch workload: the same step without
@@ -378,7 +394,9 @@ def main():
                                 f"h2o {quant_kernel} (fused step over {args.quant} codes)" if quant else
                                 f"h2o {fused_kernel} (fused attention + score + evict + insert)"),
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
-                     "kernel_source_digest": digest},
+                     "kernel_source_digest": digest,
+                     "copy_GBps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
+                     "copy_note": "plain 1 GiB device-to-device copy (read + write bytes), 5 timed"},
         "decode_head_steps_per_s": head_steps / (sum(decode_ms) / args.steps / 1e3),
         "prefill": {"ms_per_layer": pf_s * 1e3, "algorithmic_TFLOPs": prefill_flops / pf_s / 1e12,
                     "mfma_frac": prefill_flops / pf_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
