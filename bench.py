@@ -400,6 +400,10 @@ def main():
         "decode_head_steps_per_s": head_steps / (sum(decode_ms) / args.steps / 1e3),
         "prefill": {"ms_per_layer": pf_s * 1e3, "algorithmic_TFLOPs": prefill_flops / pf_s / 1e12,
                     "mfma_frac": prefill_flops / pf_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    # one causal QK^T pass is the least any exact column sum needs
+                    "one_pass_TFLOPs": 1.0 * n * (n + 1) * d * G / pf_s / 1e12,
+                    # exp2 per score in each pass: n(n+1)/2 per head and pass
+                    "exp_per_layer": float(n) * (n + 1) * G, "exp_per_s": float(n) * (n + 1) * G / pf_s,
                     "entry": args.prefill,
                     "note": ("rowattn (QK^T + P.V, prompt output) + colsum (QK^T) + select/gather + cache clear"
                              if attn else "rowlse + colsum + select/gather + cache clear, 2 causal QK^T passes")},
