@@ -65,6 +65,12 @@ def parse_args():
                         "(h2o_cache_init_quant)")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-oracle sample (0: enough for about 15 s of oracle work)")
+    p.add_argument("--policy", choices=("accumulated", "averaged", "position"), default="accumulated",
+                   help="retention value of a slot: accumulated attention (H2O), averaged attention, or position "
+                        "(sinks + window)")
+    p.add_argument("--k-heavy", type=int, default=None, help="override the workload's k_heavy (0: recent window only)")
+    p.add_argument("--k-recent", type=int, default=None,
+                   help="override the workload's k_recent (0: heavy hitters only, the new token competes)")
     p.add_argument("--fullcache", action="store_true",
                    help="also time a no-eviction decode attention over the full final length (prompt + decode "
                         "steps) on the same inputs (always on for large_batch_f16)")
@@ -127,7 +133,7 @@ def cpu_sample_heads(wl, seconds: float = 15.0) -> int:
     return int(max(1, min(wl.n_heads_total, round(seconds / per_head))))
 
 
-def cpu_baseline(wl, heads: int):
+def cpu_baseline(wl, heads: int, policy: str = "accumulated"):
     """The fp64 oracle on a bounded sample: `heads` heads, prefill plus every decode step."""
     import numpy as np
     from oracle import H2OOracle
@@ -141,7 +147,7 @@ def cpu_baseline(wl, heads: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    orc = H2OOracle(sample.size, wl.head_dim, wl.k_heavy, wl.k_recent, wl.scale)
+    orc = H2OOracle(sample.size, wl.head_dim, wl.k_heavy, wl.k_recent, wl.scale, policy)
     t0 = time.perf_counter()
     orc.prefill(Q, K, V)
     t1 = time.perf_counter()
@@ -180,6 +186,12 @@ def main():
         wl = wl.with_(steps=max(1, min(args.decode_steps, wl.steps)))
     if args.batch is not None or args.heads is not None:
         wl = wl.with_(batch=args.batch or wl.batch, heads=args.heads or wl.heads)
+    if args.k_heavy is not None or args.k_recent is not None:
+        wl = wl.with_(k_heavy=wl.k_heavy if args.k_heavy is None else args.k_heavy,
+                      k_recent=wl.k_recent if args.k_recent is None else args.k_recent)
+    policy = {"accumulated": 0, "averaged": 1, "position": 2}[args.policy]
+    default_shape = (args.batch is None and args.heads is None and args.k_heavy is None
+                     and args.k_recent is None and args.policy == "accumulated")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
@@ -235,12 +247,12 @@ def main():
         for i in layers:
             c = caches[i]
             if quant:
-                check(lib.h2o_cache_init_quant(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
+                check(lib.h2o_cache_init_quant(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, policy, dcode,
                                                ctypes.c_float(wl.scale), qcode, c.K.data_ptr(), c.V.data_ptr(),
                                                c.k_qparam.data_ptr(), c.v_qparam.data_ptr(),
                                                c.score.data_ptr(), c.pos.data_ptr(), sh))
             else:
-                check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, 0, dcode,
+                check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, policy, dcode,
                                          ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
                                          c.score.data_ptr(), c.pos.data_ptr(), sh))
             if attn:
@@ -299,7 +311,7 @@ def main():
     fused_kernel = "decode_wave_kernel" if G >= cus * 4 else "decode_kernel"
     quant_kernel = "decode_quant_kernel" if G >= cus * 4 else "decode_quant_wg_kernel"
     digest = decode_source_digest(mode)
-    traffic = load_traffic(wl.name, digest, mode) if args.batch is None and args.heads is None else None
+    traffic = load_traffic(wl.name, digest, mode) if default_shape else None
     # two causal QK^T passes per layer (d n (n+1) flops each), plus the causal P.V with the output
     prefill_flops = (3.0 if attn else 2.0) * n * (n + 1) * d * G
     pf_s = (sum(prefill_ms) / args.steps) / 1e3 / L
@@ -387,7 +399,7 @@ def main():
         "config": {"workload": wl.name, "batch": B, "heads": H, "head_dim": d, "prompt_len": n,
                    "k_heavy": wl.k_heavy, "k_recent": wl.k_recent, "decode_steps": T, "layers": L,
                    "pareto_alpha": wl.alpha, "parallelism": "none (1 GPU)", "decode_entry": args.decode,
-                   "cache_storage": f"{args.quant} codes" if quant else wl.dtype},
+                   "cache_storage": f"{args.quant} codes" if quant else wl.dtype, "policy": args.policy},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ("h2o decode_chunk_kernel + decode_merge_kernel (split decode)" if split else
@@ -413,7 +425,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads, args.policy)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
