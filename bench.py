@@ -65,6 +65,9 @@ def parse_args():
                         "(h2o_cache_init_quant)")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-oracle sample (0: enough for about 15 s of oracle work)")
+    p.add_argument("--graph", action="store_true",
+                   help="time the step as two captured HIP graphs (clear + prefill of every layer, then the decode "
+                        "steps) replayed on the stream, instead of launching each call")
     p.add_argument("--policy", choices=("accumulated", "averaged", "position"), default="accumulated",
                    help="retention value of a slot: accumulated attention (H2O), averaged attention, or position "
                         "(sinks + window)")
@@ -242,41 +245,77 @@ def main():
         if st != 0:
             raise RuntimeError(lib.h2o_last_error().decode())
 
-    def run_step(layers, ev=None):
-        """Whole path for `layers` caches: clear, prefill, T decode steps."""
+    def run_prefill(layers, h):
+        """Clear and prefill (score, select, gather) the `layers` caches."""
         for i in layers:
             c = caches[i]
             if quant:
                 check(lib.h2o_cache_init_quant(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, policy, dcode,
                                                ctypes.c_float(wl.scale), qcode, c.K.data_ptr(), c.V.data_ptr(),
                                                c.k_qparam.data_ptr(), c.v_qparam.data_ptr(),
-                                               c.score.data_ptr(), c.pos.data_ptr(), sh))
+                                               c.score.data_ptr(), c.pos.data_ptr(), h))
             else:
                 check(lib.h2o_cache_init(ctypes.byref(c.desc), B, H, d, wl.k_heavy, wl.k_recent, policy, dcode,
                                          ctypes.c_float(wl.scale), c.K.data_ptr(), c.V.data_ptr(),
-                                         c.score.data_ptr(), c.pos.data_ptr(), sh))
+                                         c.score.data_ptr(), c.pos.data_ptr(), h))
             if attn:
                 check(lib.h2o_prefill_attention(ctypes.byref(c.desc), Q.data_ptr(), K.data_ptr(), V.data_ptr(), n,
-                                                ws.data_ptr(), ws.numel(), prompt_out.data_ptr(), None, None, sh))
+                                                ws.data_ptr(), ws.numel(), prompt_out.data_ptr(), None, None, h))
             else:
                 check(lib.h2o_prefill_select(ctypes.byref(c.desc), Q.data_ptr(), K.data_ptr(), V.data_ptr(), n,
-                                             ws.data_ptr(), ws.numel(), None, sh))
-        if ev is not None:
-            ev.record(stream)
+                                             ws.data_ptr(), ws.numel(), None, h))
+
+    def run_decode(layers, h):
+        """T decode steps, the `layers` caches in rotation token by token."""
         for t in range(T):
             for i in layers:
                 if split:
                     check(lib.h2o_decode_step_split(ctypes.byref(caches[i].desc), qp[t], kp[t], vp[t],
                                                     outs[i].data_ptr(), evs[i].data_ptr(), args.chunk_rows,
-                                                    sws.data_ptr(), sws.numel(), sh))
+                                                    sws.data_ptr(), sws.numel(), h))
                 else:
                     check(lib.h2o_decode_step(ctypes.byref(caches[i].desc), qp[t], kp[t], vp[t],
-                                              outs[i].data_ptr(), evs[i].data_ptr(), sh))
+                                              outs[i].data_ptr(), evs[i].data_ptr(), h))
+
+    def run_step(layers, ev=None):
+        """Whole path for `layers` caches: clear, prefill, T decode steps."""
+        run_prefill(layers, sh)
+        if ev is not None:
+            ev.record(stream)
+        run_decode(layers, sh)
 
     all_layers = list(range(L))
     for _ in range(args.warmup):
         run_step(all_layers)
     torch.cuda.synchronize()
+
+    if args.graph:
+        # Capture once: the descriptors' host counters advance during capture,
+        # and every replay of the pair restarts from the cleared caches.
+        gstream = torch.cuda.Stream()
+        gh = ctypes.c_void_p(gstream.cuda_stream)
+        g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(gstream):
+            with torch.cuda.graph(g_pre, stream=gstream):
+                run_prefill(all_layers, gh)
+            with torch.cuda.graph(g_dec, stream=gstream):
+                run_decode(all_layers, gh)
+        torch.cuda.synchronize()
+        # The replayed step must give what the launched step gives.
+        run_step(all_layers)
+        torch.cuda.synchronize()
+        ref = [(x.clone(), y.clone()) for x, y in zip(outs, evs)]
+        g_pre.replay()
+        g_dec.replay()
+        torch.cuda.synchronize()
+        for (g_out, g_ev), (r_out, r_ev) in zip(zip(outs, evs), ref):
+            if not (torch.equal(g_out, r_out) and torch.equal(g_ev, r_ev)):
+                raise RuntimeError("graph replay differs from the launched step")
+        for _ in range(max(1, args.warmup)):
+            g_pre.replay()
+            g_dec.replay()
+        torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -285,7 +324,12 @@ def main():
     w0 = time.perf_counter()
     for s in range(args.steps):
         starts[s].record(stream)
-        run_step(all_layers, mids[s])
+        if args.graph:
+            g_pre.replay()
+            mids[s].record(stream)
+            g_dec.replay()
+        else:
+            run_step(all_layers, mids[s])
         ends[s].record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - w0
@@ -399,7 +443,8 @@ def main():
         "config": {"workload": wl.name, "batch": B, "heads": H, "head_dim": d, "prompt_len": n,
                    "k_heavy": wl.k_heavy, "k_recent": wl.k_recent, "decode_steps": T, "layers": L,
                    "pareto_alpha": wl.alpha, "parallelism": "none (1 GPU)", "decode_entry": args.decode,
-                   "cache_storage": f"{args.quant} codes" if quant else wl.dtype, "policy": args.policy},
+                   "cache_storage": f"{args.quant} codes" if quant else wl.dtype, "policy": args.policy,
+                   "launch": "graph" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": ("h2o decode_chunk_kernel + decode_merge_kernel (split decode)" if split else
