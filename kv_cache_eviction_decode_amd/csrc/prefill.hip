@@ -287,14 +287,16 @@ template <> __device__ __forceinline__ uint4 pack8<DT_F16>(const float* p) {
 // The S^T tiles are those of rowlse_lds; the probabilities of a 16-key group
 // held by a lane are exactly the 8 k values the lane supplies as the B
 // operand of O^T = V^T P^T (k slot 8h+i <-> key 16g + 8(i/4) + 4h + i%4), so P
-// never leaves registers; V^T comes from a transposed LDS tile. The online
-// softmax keeps one reference maximum per query column, shared by both lane
-// halves. It is raised only when a tile's maximum exceeds it by more than
-// kLazy (base-2 units, so probabilities stay below 2^kLazy), and the O
-// accumulators are rescaled only when some lane of the wave raised it, which
-// after the first tiles is rare. Numerator and denominator share the
-// reference, so the result is exact.
-constexpr float kLazy = 8.0f;
+// never leaves registers; V^T comes from a transposed LDS tile. The softmax
+// keeps one reference per query column, shared by both lane halves (their
+// probabilities meet in one P.V output column): as in rowlse_lds, the first
+// tile's maximum, kept while the tile's sum over both halves stays below
+// 2^64 (2^15 for fp16 inputs, whose P operand must stay finite in fp16), so
+// no maximum is taken per tile. A tile beyond that bound (or the
+// first) takes the exact path for its queries, and the O accumulators are
+// rescaled only when some lane of the wave did, which after the first tiles
+// is rare. Numerator and denominator share the reference, so the result is
+// exact up to rounding.
 
 // Workgroup of 8 waves of 32 queries sharing the K and V tiles of 256
 // queries: a wave's O accumulators (d x 32), S tile and query fragments fit in
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  float m = kNegInf, l = 0.f;
+  float ref = kNegInf, l = 0.f;
   const int ntiles = min(wg_q0 + 255, n - 1) / 64 + 1;
   uint4 nk[T::CPT], nv[T::CPT];
   T::fetch(nk, Kr, 0);
@@ -405,34 +407,52 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
               if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][j] = kNegInf;
         }
       }
-      float tm = kNegInf;
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][j], acc[0][j + 1]);
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][j], acc[1][j + 1]);
-      const float tmax = fmaxf(tm, __shfl_xor(tm, 32));
-      const bool raise = (tmax - m) * c > kLazy;
-      const float mn = raise ? tmax : m;
-      const float mnc = mn * c;
-      const float alpha = raise ? fast_exp2((m - mn) * c) : 1.0f;
-      uint4 pb[2][2];
+      // Probabilities against the query's reference (base 2, shared by the
+      // two lane halves that hold the query's keys).
+      float p[2][16];
       float t = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float p[16];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          p[j] = fast_exp2(fmaf(acc[kb][j], c, -mnc));
-          t += p[j];
+          p[kb][j] = fast_exp2(fmaf(acc[kb][j], c, -ref));
+          t += p[kb][j];
         }
-        pb[kb][0] = pack8<DT>(p);
-        pb[kb][1] = pack8<DT>(p + 8);
-      }
-      l = fmaf(l, alpha, t);
-      m = mn;
-      if (__ballot(raise)) {
+      // P feeds the MFMA in the input type: fp16 must stay below its 65504
+      // limit, bf16 has fp32's range.
+      constexpr float kBound = DT == DT_F16 ? 0x1p15f : 0x1p64f;
+      const bool redo = !(t + __shfl_xor(t, 32) <= kBound);  // first tile, far above, or NaN
+      if (__ballot(redo)) {
+        float tm = kNegInf;
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][j], acc[0][j + 1]);
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][j], acc[1][j + 1]);
+        const float tmax = fmaxf(tm, __shfl_xor(tm, 32)) * c;
+        float rn = redo ? fmaxf(ref, tmax) : ref;
+        if (rn == kNegInf) rn = 0.f;  // no visible key yet: nothing to scale
+        const float alpha = fast_exp2(ref - rn);  // 1 where the reference stays
+        if (redo) {
+          t = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              p[kb][j] = fast_exp2(fmaf(acc[kb][j], c, -rn));
+              t += p[kb][j];
+            }
+        }
+        l *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        ref = rn;
+      }
+      l += t;
+      uint4 pb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        pb[kb][0] = pack8<DT>(p[kb]);
+        pb[kb][1] = pack8<DT>(p[kb] + 8);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -452,7 +472,7 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
   for (int kt = nfull; kt < ntiles; ++kt) step(kt, std::true_type{});
   const float lt = l + __shfl_xor(l, 32);  // both halves share the reference maximum
   if (qi < n) {
-    const float lse2 = m * c + fast_log2(lt);
+    const float lse2 = ref + fast_log2(lt);
     if (lh == 0) {
       a.lse2[size_t(head) * ld_lse + qi] = lse2;
       if (a.lse_out) a.lse_out[size_t(head) * n + qi] = lse2 * 0.6931471805599453f;
