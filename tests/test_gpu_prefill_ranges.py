@@ -43,6 +43,7 @@ CASES = [
     ("bf16_2wave", "bf16", 128, 700, [(300, 2.0), (500, 8.0), (650, 16.0)]),
     ("f16_2wave_d64", "f16", 64, 600, [(130, 4.0), (400, 16.0), (599, 32.0)]),
     ("bf16_4wave", "bf16", 128, 2300, [(700, 2.0), (1500, 8.0), (2100, 16.0)]),
+    ("f16_4wave", "f16", 128, 2300, [(700, 2.0), (1500, 8.0), (2100, 16.0)]),
 ]
 
 

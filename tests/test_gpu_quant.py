@@ -61,6 +61,18 @@ def test_quant_opt_layer_full_size(gpu, quant):
 
 
 @pytest.mark.parametrize("quant", FORMATS)
+def test_quant_wave_kernel_beyond_prefetch(gpu, quant):
+    """1024 heads (one wave per head) with 320 slots: the scores and positions
+    past the 256 prefetched per head are read in the epilogue."""
+    wl = Workload("quant_wave_320", 32, 32, 128, "bf16", 400, 160, 160, 10, 1.5, 0.0, 91)
+    run = ParityRun(wl, wl.steps, sample=sample_heads(wl, 8), quant=quant)
+    run.prefill()
+    rep = run.decode()
+    log(f"[{quant}] wave kernel, 320 slots: {rep}")
+    assert rep.steps == wl.steps
+
+
+@pytest.mark.parametrize("quant", FORMATS)
 def test_quant_errors(gpu, quant):
     from kv_cache_eviction_decode_amd import H2OCache, binding as b
     c = H2OCache(1, 2, 128, 8, 8, torch.bfloat16, device="cuda", quant=quant)
