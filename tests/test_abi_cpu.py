@@ -1,11 +1,14 @@
 """The C-ABI library loads on a machine without a GPU, exports every declared
 entry point, and rejects bad arguments before touching the device (CPU only)."""
 import ctypes
+import os
 import re
 
 import pytest
 
 from kv_cache_eviction_decode_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_functions():
@@ -129,3 +132,31 @@ def test_fullcache_rejects_bad_arguments():
 def test_raised_error_carries_library_message():
     with pytest.raises(b.H2OError, match="H2O_ESTATE"):
         b.h2o_cache_restore(b.h2o_cache(), 1)
+
+
+def test_missing_library_fails_loudly():
+    """Without the built HIP library the binding raises; there is no fallback path."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from kv_cache_eviction_decode_amd import binding\n"
+            "try:\n"
+            "    binding.load_library('/nonexistent/libh2o.so')\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n"
+            "else:\n"
+            "    sys.exit(3)\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "raised" in r.stdout
+
+
+def test_package_does_not_import_the_oracle():
+    """The product package never loads the test oracle."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import kv_cache_eviction_decode_amd\n"
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]\n"
+            "sys.exit(1 if bad else 0)\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
