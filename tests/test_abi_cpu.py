@@ -160,3 +160,11 @@ def test_package_does_not_import_the_oracle():
             "sys.exit(1 if bad else 0)\n") % ROOT
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
+
+
+def test_build_compiles_every_kernel_source():
+    """Every .hip file of the package is part of the library build."""
+    import glob
+    from kv_cache_eviction_decode_amd import build
+    on_disk = sorted(os.path.basename(p) for p in glob.glob(os.path.join(build.CSRC, "*.hip")))
+    assert on_disk == sorted(build.SOURCES)
