@@ -167,12 +167,12 @@ def _golden_inputs(g):
     return n, steps, qs, keys, vals, scale
 
 
-@pytest.mark.parametrize("name", ["illustration_budget3.txt", "weighted_budget3.txt"])
+@pytest.mark.parametrize("name", ["illustration_budget3.txt", "weighted_budget3.txt", "averaged_budget3.txt"])
 def test_golden_hand_worked(name):
     g = _load_golden(name)
     n, steps, qs, keys, vals, scale = _golden_inputs(g)
     d = qs.shape[1]
-    orc = H2OOracle(1, d, int(g["k_heavy"]), int(g["k_recent"]), scale)
+    orc = H2OOracle(1, d, int(g["k_heavy"]), int(g["k_recent"]), scale, g.get("policy", "accumulated"))
     pre = orc.prefill(qs[None, :n], keys[None, :n], vals[None, :n])
     np.testing.assert_allclose(pre.colsum[0], _fracs(g["colsum"]), rtol=1e-13)
     assert orc.pos[0].tolist() == [int(x) for x in g["after_prefill_pos"].split()]
@@ -183,6 +183,19 @@ def test_golden_hand_worked(name):
         np.testing.assert_allclose(st.out[0], _fracs(g[f"step{t}_out"]), rtol=1e-13)
     assert orc.pos[0].tolist() == [int(x) for x in g["final_pos"].split()]
     np.testing.assert_allclose(orc.score[0], _fracs(g["final_score"]), rtol=1e-13)
+
+
+def test_averaged_fixture_discriminates():
+    """On the averaged fixture's inputs accumulated attention keeps position 0
+    at prefill and evicts 4 at the third step, so the fixture pins the averaging."""
+    g = _load_golden("averaged_budget3.txt")
+    n, steps, qs, keys, vals, scale = _golden_inputs(g)
+    orc = H2OOracle(1, 1, int(g["k_heavy"]), int(g["k_recent"]), scale, "accumulated")
+    orc.prefill(qs[None, :n], keys[None, :n], vals[None, :n])
+    assert orc.pos[0].tolist() == [0, 2, 3]
+    ev = [int(orc.decode_step(qs[None, n + t], keys[None, n + t], vals[None, n + t]).evicted[0])
+          for t in range(steps)]
+    assert ev[2] == 4
 
 
 # ----------------------------------------------------------------------------- textbook special cases
