@@ -73,6 +73,54 @@ def test_quant_wave_kernel_beyond_prefetch(gpu, quant):
 
 
 @pytest.mark.parametrize("quant", FORMATS)
+def test_quant_uniform_closed_form_full_shape(gpu, quant):
+    """All-zero queries at the OPT-6.7B layer shape over a cache of codes:
+    every logit is 0 whatever the key codes, so the column sums are harmonic
+    differences, the selection is the first k_heavy plus the window, and every
+    step evicts t - k_recent. Each output is the mean of the cached values as
+    stored, so it lies within the largest half grid step of its rows of the
+    mean of the exact values (the new token attends at full precision)."""
+    import numpy as np
+    from h2o_harness import to_device
+    from kv_cache_eviction_decode_amd import H2OCache
+    from workload import make_decode, make_prompt
+    wl = WORKLOADS["opt6.7b_layer"]
+    B, H, d, n, kh, kr = wl.batch, wl.heads, wl.head_dim, wl.prompt_len, wl.k_heavy, wl.k_recent
+    T = 16
+    levels = {"u8": 255, "u4": 15, "u2": 3}[quant]
+    dev = torch.device("cuda")
+    _, K, V = make_prompt(wl)
+    _, kd, vd = make_decode(wl, steps=T)
+    cache = H2OCache(B, H, d, kh, kr, torch.bfloat16, wl.scale, dev, quant=quant)
+    Qz = torch.zeros(B, H, n, d, dtype=torch.bfloat16, device=dev)
+    colsum = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    cache.prefill_select(Qz, to_device(K, "bf16", dev).view(B, H, n, d), to_device(V, "bf16", dev).view(B, H, n, d),
+                         colsum_out=colsum)
+    Hn = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    np.testing.assert_allclose(colsum.cpu().numpy().reshape(-1, n), np.broadcast_to(Hn[n] - Hn[:n], (B * H, n)),
+                               rtol=1e-4)
+    expect = np.array(list(range(kh)) + list(range(n - kr, n)), dtype=np.int32)
+    assert (cache.pos.cpu().numpy().reshape(-1, wl.k) == expect).all()
+    allv = np.concatenate([V, vd], axis=1).astype(np.float64)  # [G, n+T, d]
+    half_step = (allv.max(axis=2) - allv.min(axis=2)) / levels / 2  # per row
+    members = np.broadcast_to(expect, (B * H, wl.k)).copy()
+    qz = torch.zeros(B, H, d, dtype=torch.bfloat16, device=dev)
+    kdg = to_device(kd.transpose(1, 0, 2), "bf16", dev).view(T, B, H, d)
+    vdg = to_device(vd.transpose(1, 0, 2), "bf16", dev).view(T, B, H, d)
+    for t in range(T):
+        out, ev = cache.decode_step(qz, kdg[t], vdg[t])
+        pos_t = n + t
+        assert (ev.cpu().numpy() == pos_t - kr).all(), f"step {t}"
+        idx = np.concatenate([members, np.full((B * H, 1), pos_t)], axis=1)
+        mean = np.take_along_axis(allv, idx[:, :, None], axis=1).mean(axis=1)
+        bound = np.take_along_axis(half_step, members, axis=1).max(axis=1) + 1e-5
+        err = np.abs(out.cpu().numpy().reshape(B * H, d) - mean).max(axis=1)
+        assert (err <= bound).all(), f"step {t}: {err.max()} > {bound[err.argmax()]}"
+        members[members == pos_t - kr] = pos_t
+    log(f"[{quant}] uniform closed form at full shape: {T} steps")
+
+
+@pytest.mark.parametrize("quant", FORMATS)
 def test_quant_errors(gpu, quant):
     from kv_cache_eviction_decode_amd import H2OCache, binding as b
     c = H2OCache(1, 2, 128, 8, 8, torch.bfloat16, device="cuda", quant=quant)
