@@ -78,3 +78,46 @@ def test_split_errors(gpu):
     c.decode_step_split(q, q, q, out, ev)
     torch.cuda.synchronize()
     assert c.t_next == 1 and ev.tolist() == [[-1, -1]]
+
+
+def test_split_uniform_closed_form(gpu):
+    """All-zero queries through the split entry point at the long-context shape
+    with one sequence (32 heads x 2048 slots, the library's chunking): column
+    sums are harmonic differences, the selection is the first k_heavy tokens
+    plus the window, every step evicts t - k_recent and each output is the
+    plain mean of the cached values and the new one."""
+    import numpy as np
+    from h2o_harness import to_device
+    from kv_cache_eviction_decode_amd import H2OCache
+    from workload import make_decode, make_prompt
+    wl = WORKLOADS["long_context"].with_(batch=1)
+    B, H, d, n, kh, kr = wl.batch, wl.heads, wl.head_dim, wl.prompt_len, wl.k_heavy, wl.k_recent
+    T = 8
+    dev = torch.device("cuda")
+    _, K, V = make_prompt(wl)
+    _, kd, vd = make_decode(wl, steps=T)
+    cache = H2OCache(B, H, d, kh, kr, torch.bfloat16, wl.scale, dev)
+    colsum = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    cache.prefill_select(torch.zeros(B, H, n, d, dtype=torch.bfloat16, device=dev),
+                         to_device(K, "bf16", dev).view(B, H, n, d), to_device(V, "bf16", dev).view(B, H, n, d),
+                         colsum_out=colsum)
+    Hn = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    np.testing.assert_allclose(colsum.cpu().numpy().reshape(-1, n), np.broadcast_to(Hn[n] - Hn[:n], (B * H, n)),
+                               rtol=1e-4)
+    expect = np.array(list(range(kh)) + list(range(n - kr, n)), dtype=np.int32)
+    assert (cache.pos.cpu().numpy().reshape(-1, wl.k) == expect).all()
+    allv = np.concatenate([V, vd], axis=1).astype(np.float64)
+    members = np.broadcast_to(expect, (B * H, wl.k)).copy()
+    qz = torch.zeros(B, H, d, dtype=torch.bfloat16, device=dev)
+    kdg = to_device(kd.transpose(1, 0, 2), "bf16", dev).view(T, B, H, d)
+    vdg = to_device(vd.transpose(1, 0, 2), "bf16", dev).view(T, B, H, d)
+    for t in range(T):
+        out, ev = cache.decode_step_split(qz, kdg[t], vdg[t])
+        pos_t = n + t
+        assert (ev.cpu().numpy() == pos_t - kr).all(), f"step {t}"
+        idx = np.concatenate([members, np.full((B * H, 1), pos_t)], axis=1)
+        mean = np.take_along_axis(allv, idx[:, :, None], axis=1).mean(axis=1)
+        err = np.abs(out.cpu().numpy().reshape(B * H, d) - mean).max()
+        assert err <= 1e-5, f"step {t}: {err}"
+        members[members == pos_t - kr] = pos_t
+    log(f"[split] uniform closed form, 32 heads x {wl.k} slots: {T} steps")
