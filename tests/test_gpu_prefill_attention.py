@@ -59,3 +59,40 @@ def test_prefill_attention_full_size(gpu, name, nsample):
     rep = run.decode()
     log(f"[prefill attention] {name} full size: {rep}")
     assert rep.steps == 8
+
+
+@pytest.mark.parametrize("dtype,n,batch", [("bf16", 1024, 64), ("f16", 2300, 16)])
+def test_prefill_attention_zero_queries_closed_form(gpu, dtype, n, batch):
+    """All-zero queries: every causal row is uniform, so the prompt's output row
+    i is the running mean of V_0..V_i and its log normaliser is ln(i + 1); the
+    column sums are harmonic differences. Checked on a sample of heads at the
+    OPT-6.7B head count (2-wave prefill at n = 1024, 4-wave at 2300)."""
+    import numpy as np
+    import torch
+    from h2o_harness import TORCH_DTYPE, to_device
+    from kv_cache_eviction_decode_amd import H2OCache
+    from workload import make_prompt, sample_heads
+    wl = WORKLOADS["opt6.7b_layer"].with_(dtype=dtype, prompt_len=n, batch=batch)
+    B, H, d = wl.batch, wl.heads, wl.head_dim
+    dev = torch.device("cuda")
+    sample = sample_heads(wl, 6)
+    _, K, V = make_prompt(wl)
+    cache = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, TORCH_DTYPE[dtype], wl.scale, dev)
+    lse = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    colsum = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    out = cache.prefill_attention(torch.zeros(B, H, n, d, dtype=TORCH_DTYPE[dtype], device=dev),
+                                  to_device(K, dtype, dev).view(B, H, n, d), to_device(V, dtype, dev).view(B, H, n, d),
+                                  lse_out=lse, colsum_out=colsum)
+    idx = torch.from_numpy(sample).to(dev)
+    gout = out.view(-1, n, d).index_select(0, idx).cpu().numpy()
+    glse = lse.view(-1, n).index_select(0, idx).cpu().numpy()
+    gcol = colsum.view(-1, n).index_select(0, idx).cpu().numpy()
+    rows = np.arange(1, n + 1, dtype=np.float64)
+    Hn = np.concatenate([[0.0], np.cumsum(1.0 / rows)])
+    for j, g in enumerate(sample):
+        mean = np.cumsum(V[g].astype(np.float64), axis=0) / rows[:, None]
+        err = float(np.abs(gout[j] - mean).max())
+        assert err <= 2e-2, f"head {g}: output err {err:.3g}"
+        np.testing.assert_allclose(glse[j], np.log(rows), rtol=1e-5, atol=1e-5)
+        np.testing.assert_allclose(gcol[j], Hn[n] - Hn[:n], rtol=1e-4)
+    log(f"[attention] zero queries, {dtype} n={n}: closed form holds on {sample.size} heads")
