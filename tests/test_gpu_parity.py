@@ -274,3 +274,41 @@ def test_window_policies_are_textbook_attention(gpu, policy, kh, kr):
             # inputs are the exact bf16 values on both sides: only fp32 sums and exp2 differ
             assert err <= 1e-4, f"step {t} head {g}: {err:.3g}"
     log(f"[parity] {policy} kh={kh} kr={kr}: textbook attention over {T} steps")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_never_full_cache_is_causal_attention(gpu, dtype):
+    """k >= n + T: nothing is ever evicted, so each decode output is causal
+    attention over the whole sequence so far and the final scores are the
+    column sums of the full causal attention matrix (prompt and decode rows),
+    computed here directly in float64 from the same 16-bit inputs."""
+    wl = Workload("never_full", 2, 8, 128, dtype, 300, 256, 256, 20, 1.5, 0.0, 47)
+    B, H, d, n, T = wl.batch, wl.heads, wl.head_dim, wl.prompt_len, wl.steps
+    G, N = B * H, n + T
+    dev = torch.device("cuda")
+    from kv_cache_eviction_decode_amd import H2OCache
+    Q, K, V = make_prompt(wl)
+    qd, kd, vd = make_decode(wl)
+    cache = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, TORCH_DTYPE[dtype], wl.scale, dev)
+    cache.prefill_select(*(to_device(x, dtype, dev).view(B, H, n, d) for x in (Q, K, V)))
+    stage = lambda a: to_device(a.transpose(1, 0, 2), dtype, dev).view(T, B, H, d)
+    qg, kg, vg = stage(qd), stage(kd), stage(vd)
+    allq = np.concatenate([Q, qd], axis=1).astype(np.float64)
+    allk = np.concatenate([K, kd], axis=1).astype(np.float64)
+    allv = np.concatenate([V, vd], axis=1).astype(np.float64)
+    S = wl.scale * np.einsum("gid,gjd->gij", allq, allk)
+    S = np.where(np.tril(np.ones((N, N), dtype=bool)), S, -np.inf)
+    P = np.exp(S - S.max(axis=2, keepdims=True))
+    P /= P.sum(axis=2, keepdims=True)
+    for t in range(T):
+        out, ev = cache.decode_step(qg[t], kg[t], vg[t])
+        assert (ev.cpu().numpy() == -1).all()
+        ref = np.einsum("gj,gjd->gd", P[:, n + t], allv)
+        err = float(np.abs(out.cpu().numpy().reshape(G, d) - ref).max())
+        assert err <= 1e-4, f"step {t}: {err:.3g}"
+    assert cache.n_used == N
+    pos = cache.pos.cpu().numpy().reshape(G, -1)
+    assert (pos[:, :N] == np.arange(N)).all() and (pos[:, N:] == -1).all()
+    score = cache.score.cpu().numpy().reshape(G, -1)[:, :N]
+    np.testing.assert_allclose(score, P.sum(axis=1), rtol=1e-4)
+    log(f"[parity] never-full {dtype}: causal attention and column sums over {N} positions")
