@@ -33,6 +33,10 @@ SMALL = [
     # leaves whole waves past the prompt (2100) or one wave partly inside (2500)
     ("ragged_4wave_bf16", 1, 2, 128, "bf16", 2100, 64, 64, 8, 1.5, 0.0),
     ("ragged_4wave_f16_d64", 1, 1, 64, "f16", 2500, 30, 31, 6, 1.2, 0.0),
+    # whole 64-row tiles, but not whole workgroups: the last workgroup's later
+    # waves lie past the prompt while its last tile is full
+    ("tile_multiple_2wave_f16_d64", 1, 2, 64, "f16", 192, 32, 32, 8, 1.5, 0.0),
+    ("tile_multiple_4wave_bf16", 1, 2, 128, "bf16", 2112, 64, 64, 6, 1.5, 0.0),
 ]
 
 
