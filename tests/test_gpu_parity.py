@@ -316,3 +316,45 @@ def test_never_full_cache_is_causal_attention(gpu, dtype):
     score = cache.score.cpu().numpy().reshape(G, -1)[:, :N]
     np.testing.assert_allclose(score, P.sum(axis=1), rtol=1e-4)
     log(f"[parity] never-full {dtype}: causal attention and column sums over {N} positions")
+
+
+def test_reinitialised_cache_equals_fresh(gpu):
+    """A cache re-initialised after a prefill and some decode steps of one
+    prompt, then run on another, gives bit for bit what a fresh cache gives."""
+    from kv_cache_eviction_decode_amd import H2OCache
+    dev = torch.device("cuda")
+    a = Workload("reinit_a", 2, 4, 128, "bf16", 400, 40, 40, 30, 1.5, 0.0, 61)
+    b = a.with_(name="reinit_b", prompt_len=333, seed=62)
+    B, H, d = a.batch, a.heads, a.head_dim
+
+    def inputs(wl):
+        Q, K, V = make_prompt(wl)
+        qd, kd, vd = make_decode(wl)
+        n = wl.prompt_len
+        P = [to_device(x, "bf16", dev).view(B, H, n, d) for x in (Q, K, V)]
+        D = [to_device(x.transpose(1, 0, 2), "bf16", dev).view(wl.steps, B, H, d) for x in (qd, kd, vd)]
+        return P, D
+
+    def run(cache, wl, steps):
+        P, D = inputs(wl)
+        cache.prefill_select(*P)
+        outs = []
+        for t in range(steps):
+            out, ev = cache.decode_step(D[0][t], D[1][t], D[2][t])
+            outs.append((out.clone(), ev.clone()))
+        torch.cuda.synchronize()
+        return outs
+
+    used = H2OCache(B, H, d, a.k_heavy, a.k_recent, torch.bfloat16, a.scale, dev)
+    run(used, a, 17)
+    from kv_cache_eviction_decode_amd.binding import h2o_cache_init
+    h2o_cache_init(used.desc, B, H, d, a.k_heavy, a.k_recent, "accumulated", a.scale,
+                   used.K, used.V, used.score, used.pos, None)
+    got = run(used, b, b.steps)
+    fresh = H2OCache(B, H, d, a.k_heavy, a.k_recent, torch.bfloat16, a.scale, dev)
+    want = run(fresh, b, b.steps)
+    for t, ((go, ge), (wo, we)) in enumerate(zip(got, want)):
+        assert torch.equal(go, wo) and torch.equal(ge, we), f"step {t}"
+    for x, y in ((used.K, fresh.K), (used.V, fresh.V), (used.score, fresh.score), (used.pos, fresh.pos)):
+        assert torch.equal(x, y)
+    log("[parity] re-initialised cache equals a fresh one")
