@@ -358,3 +358,45 @@ def test_reinitialised_cache_equals_fresh(gpu):
     for x, y in ((used.K, fresh.K), (used.V, fresh.V), (used.score, fresh.score), (used.pos, fresh.pos)):
         assert torch.equal(x, y)
     log("[parity] re-initialised cache equals a fresh one")
+
+
+def test_two_caches_on_two_streams(gpu):
+    """Two caches decoded concurrently on two streams (default priority) give
+    bit for bit what the same calls give one after the other on one stream:
+    the library keeps no state shared between calls."""
+    from kv_cache_eviction_decode_amd import H2OCache
+    dev = torch.device("cuda")
+    wls = [Workload("streams_a", 4, 8, 128, "bf16", 500, 64, 64, 24, 1.5, 0.0, 71),
+           Workload("streams_b", 4, 8, 128, "bf16", 700, 64, 64, 24, 1.2, 0.0, 72)]
+    data = []
+    for wl in wls:
+        Q, K, V = make_prompt(wl)
+        qd, kd, vd = make_decode(wl)
+        B, H, n, d = wl.batch, wl.heads, wl.prompt_len, wl.head_dim
+        data.append(([to_device(x, "bf16", dev).view(B, H, n, d) for x in (Q, K, V)],
+                     [to_device(x.transpose(1, 0, 2), "bf16", dev).view(wl.steps, B, H, d) for x in (qd, kd, vd)]))
+
+    def run(streams):
+        caches = [H2OCache(wl.batch, wl.heads, wl.head_dim, wl.k_heavy, wl.k_recent, torch.bfloat16, wl.scale, dev)
+                  for wl in wls]
+        outs = [torch.empty(wls[0].steps, wl.batch, wl.heads, wl.head_dim, device=dev) for wl in wls]
+        evs = [torch.empty(wls[0].steps, wl.batch, wl.heads, dtype=torch.int32, device=dev) for wl in wls]
+        torch.cuda.synchronize()
+        for i, (c, (P, D)) in enumerate(zip(caches, data)):
+            with torch.cuda.stream(streams[i]):
+                c.prefill_select(*P, stream=streams[i])
+        for t in range(wls[0].steps):
+            for i, (c, (P, D)) in enumerate(zip(caches, data)):
+                with torch.cuda.stream(streams[i]):
+                    c.decode_step(D[0][t], D[1][t], D[2][t], outs[i][t], evs[i][t], stream=streams[i])
+        torch.cuda.synchronize()
+        return outs, evs, caches
+
+    s0 = torch.cuda.current_stream()
+    seq = run([s0, s0])
+    par = run([torch.cuda.Stream(), torch.cuda.Stream()])
+    for i in range(2):
+        assert torch.equal(seq[0][i], par[0][i]) and torch.equal(seq[1][i], par[1][i])
+        for x, y in ((seq[2][i].score, par[2][i].score), (seq[2][i].pos, par[2][i].pos), (seq[2][i].K, par[2][i].K)):
+            assert torch.equal(x, y)
+    log("[parity] two caches on two streams match one stream")
