@@ -92,3 +92,57 @@ def test_decode_steps_replay_from_a_graph(gpu, mode):
             assert torch.equal(a, b), f"replay {rep}: cache state differs"
         # eager work between replays
         _ = (outs * 2).sum().item()
+
+
+@pytest.mark.parametrize("mode", ["select", "attention", "u4"])
+def test_init_and_prefill_replay_from_a_graph(gpu, mode):
+    """Cache initialisation and prefill (clear kernel, scoring passes,
+    selection and gather; for "attention" also the prompt's output) captured
+    once and replayed three times, with eager work between the replays: every
+    replay reproduces the eager result bit for bit."""
+    from kv_cache_eviction_decode_amd.binding import h2o_cache_init, h2o_cache_init_quant
+    wl = Workload("graph_prefill_" + mode, 2, 4, 128, "bf16", 700, 40, 40, T, 1.5, 0.0, seed=57)
+    dev = torch.device("cuda")
+    P, _ = _inputs(wl, dev)
+    B, H, d, n = wl.batch, wl.heads, wl.head_dim, wl.prompt_len
+    quant = "u4" if mode == "u4" else None
+    c = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, torch.bfloat16, wl.scale, dev, quant=quant)
+    c.workspace(n)
+    colsum = torch.empty(B, H, n, dtype=torch.float32, device=dev)
+    pout = torch.empty(B, H, n, d, dtype=torch.float32, device=dev)
+
+    def step(stream=None):
+        if quant:
+            h2o_cache_init_quant(c.desc, B, H, d, wl.k_heavy, wl.k_recent, "accumulated", torch.bfloat16, wl.scale,
+                                 quant, c.K, c.V, c.k_qparam, c.v_qparam, c.score, c.pos, stream)
+        else:
+            h2o_cache_init(c.desc, B, H, d, wl.k_heavy, wl.k_recent, "accumulated", wl.scale,
+                           c.K, c.V, c.score, c.pos, stream)
+        if mode == "attention":
+            c.prefill_attention(*P, out=pout, colsum_out=colsum, stream=stream)
+        else:
+            c.prefill_select(*P, colsum_out=colsum, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in _state(c) + [colsum, pout]]
+
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in _state(c):
+            x.zero_()
+        colsum.fill_(float("nan"))
+        if mode == "attention":
+            pout.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(_state(c) + [colsum, pout], ref):
+            assert torch.equal(a, b), f"replay {rep}: state differs"
+        _ = (colsum * 2).sum().item()  # eager work between replays
