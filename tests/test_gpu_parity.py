@@ -400,3 +400,36 @@ def test_two_caches_on_two_streams(gpu):
         for x, y in ((seq[2][i].score, par[2][i].score), (seq[2][i].pos, par[2][i].pos), (seq[2][i].K, par[2][i].K)):
             assert torch.equal(x, y)
     log("[parity] two caches on two streams match one stream")
+
+
+def test_maximum_prompt_closed_form(gpu):
+    """One head at the largest prompt the library accepts (H2O_MAX_PROMPT), with
+    all-zero queries: the column sums are the harmonic differences H_n - H_j
+    at every position, the selection is the first k_heavy plus the window, and
+    decode evicts t - k_recent. Exercises every prefill tile and the largest
+    row offsets the kernels address."""
+    from kv_cache_eviction_decode_amd import H2OCache
+    from kv_cache_eviction_decode_amd.binding import H2O_MAX_PROMPT
+    n = H2O_MAX_PROMPT
+    wl = Workload("max_prompt", 1, 1, 128, "bf16", n, 1024, 1024, 4, 1.5, 0.0, 83)
+    d, kh, kr = wl.head_dim, wl.k_heavy, wl.k_recent
+    dev = torch.device("cuda")
+    _, K, V = make_prompt(wl)
+    _, kd, vd = make_decode(wl)
+    cache = H2OCache(1, 1, d, kh, kr, torch.bfloat16, wl.scale, dev)
+    colsum = torch.empty(1, 1, n, dtype=torch.float32, device=dev)
+    log(f"[parity] max prompt: prefill of {n} tokens")
+    cache.prefill_select(torch.zeros(1, 1, n, d, dtype=torch.bfloat16, device=dev),
+                         to_device(K, "bf16", dev).view(1, 1, n, d), to_device(V, "bf16", dev).view(1, 1, n, d),
+                         colsum_out=colsum)
+    del K, V
+    Hn = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1, dtype=np.float64))])
+    np.testing.assert_allclose(colsum.view(-1).cpu().numpy(), Hn[n] - Hn[:n], rtol=1e-4)
+    expect = np.array(list(range(kh)) + list(range(n - kr, n)), dtype=np.int32)
+    assert (cache.pos.view(-1).cpu().numpy() == expect).all()
+    qz = torch.zeros(1, 1, d, dtype=torch.bfloat16, device=dev)
+    for t in range(wl.steps):
+        _, ev = cache.decode_step(qz, to_device(kd[:, t], "bf16", dev).view(1, 1, d),
+                                  to_device(vd[:, t], "bf16", dev).view(1, 1, d))
+        assert int(ev.item()) == n + t - kr, f"step {t}"
+    log("[parity] max prompt: closed form holds")
