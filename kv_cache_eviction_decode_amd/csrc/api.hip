@@ -30,8 +30,6 @@ h2o_status device_status(hipError_t e, const char* where) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int elem_bytes(int32_t dtype) { return dtype == H2O_F32 ? 4 : 2; }
-
 // Bits per code of a quantised cache.
 int code_bits(int32_t quant) { return quant == H2O_QUANT_U8 ? 8 : quant == H2O_QUANT_U4 ? 4 : 2; }
 
