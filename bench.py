@@ -181,8 +181,12 @@ def main():
     import torch
 
     from kv_cache_eviction_decode_amd import H2OCache, load_library
+    from kv_cache_eviction_decode_amd.binding import LIB_PATH
     from workload import ELEM_BYTES, WORKLOADS, make_decode, make_prompt
 
+    if not os.path.exists(LIB_PATH):  # use an existing build; build only if there is none
+        from kv_cache_eviction_decode_amd.build import build
+        build()
     lib = load_library()
     wl = WORKLOADS[args.workload]
     if args.decode_steps is not None:

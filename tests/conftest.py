@@ -28,3 +28,13 @@ def gpu():
     if not gpu_available():
         pytest.fail("GPU test selected but no GPU is visible to torch")
     return True
+
+
+@pytest.fixture(scope="session", autouse=True)
+def built_library():
+    """Build the HIP library once if it is not there (it is not committed);
+    an existing build is used as it is."""
+    from kv_cache_eviction_decode_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from kv_cache_eviction_decode_amd.build import build
+        build()
