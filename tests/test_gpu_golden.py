@@ -58,7 +58,8 @@ def _inputs(g):
     return n, d, steps, q, k, v, scale
 
 
-@pytest.mark.parametrize("name", ["illustration_budget3.txt", "weighted_budget3.txt", "averaged_budget3.txt"])
+@pytest.mark.parametrize("name", ["illustration_budget3.txt", "weighted_budget3.txt", "averaged_budget3.txt",
+                                  "heavy_only_budget2.txt"])
 def test_golden_on_gpu(gpu, name):
     g = _load(name)
     n, d, steps, q, k, v, scale = _inputs(g)

@@ -167,7 +167,8 @@ def _golden_inputs(g):
     return n, steps, qs, keys, vals, scale
 
 
-@pytest.mark.parametrize("name", ["illustration_budget3.txt", "weighted_budget3.txt", "averaged_budget3.txt"])
+@pytest.mark.parametrize("name", ["illustration_budget3.txt", "weighted_budget3.txt", "averaged_budget3.txt",
+                                  "heavy_only_budget2.txt"])
 def test_golden_hand_worked(name):
     g = _load_golden(name)
     n, steps, qs, keys, vals, scale = _golden_inputs(g)
