@@ -181,12 +181,10 @@ def main():
     import torch
 
     from kv_cache_eviction_decode_amd import H2OCache, load_library
-    from kv_cache_eviction_decode_amd.binding import LIB_PATH
+    from kv_cache_eviction_decode_amd.build import ensure_built
     from workload import ELEM_BYTES, WORKLOADS, make_decode, make_prompt
 
-    if not os.path.exists(LIB_PATH):  # use an existing build; build only if there is none
-        from kv_cache_eviction_decode_amd.build import build
-        build()
+    ensure_built()  # builds only if no build of the current sources exists
     lib = load_library()
     wl = WORKLOADS[args.workload]
     if args.decode_steps is not None:
@@ -456,6 +454,7 @@ def main():
                                 f"h2o {fused_kernel} (fused attention + score + evict + insert)"),
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_launch_s * 1e6,
                      "kernel_source_digest": digest,
+                     "library_digest": lib.h2o_build_digest().decode(),
                      "copy_GBps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
                      "copy_note": "plain 1 GiB device-to-device copy (read + write bytes), 5 timed"},
         "decode_head_steps_per_s": head_steps / (sum(decode_ms) / args.steps / 1e3),

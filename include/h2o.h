@@ -41,6 +41,7 @@ extern "C" {
 
 typedef void* h2o_stream_t; /* a hipStream_t */
 
+/* Status codes are small positive integers (0 = success). */
 typedef enum {
   H2O_OK = 0,
   H2O_EINVAL = 1,     /* null pointer, bad size, unsupported dtype or head dim */
@@ -119,10 +120,11 @@ typedef struct {
   int64_t steps;    /* decode steps taken since init */
   uint32_t magic;   /* set by h2o_cache_init */
   int32_t quant;    /* h2o_quant */
-  float* k_qparam;  /* U8 only: [batch][heads][2][head_dim] fp32, key grid scale_c then mn_c */
-  float* v_qparam;  /* U8 only: [batch][heads][k][2] fp32, value grid (scale, mn) of each slot */
+  float* k_qparam;  /* U8/U4/U2 only (NULL otherwise): [batch][heads][2][head_dim] fp32, key grid scale_c then mn_c */
+  float* v_qparam;  /* U8/U4/U2 only (NULL otherwise): [batch][heads][k][2] fp32, value grid (scale, mn) of each slot */
 } h2o_cache;
 
+/* Host view of a cache's counters (see h2o_cache_state). */
 typedef struct {
   int32_t n_used, t_next, k, k_heavy, k_recent;
   int32_t reserved;
@@ -164,13 +166,13 @@ h2o_status h2o_cache_init_quant(h2o_cache* cache, int32_t batch, int32_t heads, 
                                 float scale, int32_t quant, uint8_t* Kq, uint8_t* Vq, float* k_qparam,
                                 float* v_qparam, float* score, int32_t* pos, h2o_stream_t stream);
 
-/* h2o_cache_init_quant with quant = H2O_QUANT_U8. */
-h2o_status h2o_cache_init_u8(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
-                             int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype,
-                             float scale, uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam,
-                             float* score, int32_t* pos, h2o_stream_t stream);
-
-/* Bytes of device workspace h2o_prefill_select needs for a prompt of n tokens. */
+/*
+ * Bytes of device workspace h2o_prefill_select, h2o_prefill_attention and
+ * h2o_prefill_select_lse need for a prompt of n tokens (0 for an invalid
+ * shape): each prompt row's log normaliser, then the column sums when the
+ * caller does not ask for them. Sizing only: the pages describe no memory
+ * layout, so no passage defines this call.
+ */
 size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n);
 
 /*
@@ -226,7 +228,11 @@ h2o_status h2o_prefill_select_lse(h2o_cache* cache, const void* Q, const void* K
  * attention" then "Cache eviction"; H2O §2 "Problem formulation"):
  *   q, k_new, v_new : [batch][heads][head_dim] dtype, the new token
  *   out             : [batch][heads][head_dim] fp32, attention output
- *   evicted_pos     : [batch][heads] int32, evicted position or -1
+ *   evicted_pos     : [batch][heads] int32, the evicted position; -1 when
+ *                     the cache was not full; -2 when it was full but no slot
+ *                     was eligible, which a cache driven only through this
+ *                     interface never is (a caller that rewrote pos
+ *                     inconsistently): then no slot is written
  * 1. p = softmax over the occupied slots plus the new token itself of scale*q.k.
  * 2. out = sum p_a V_a + p_new v_new.
  * 3. score_a += p_a for every occupied slot.
@@ -238,6 +244,12 @@ h2o_status h2o_prefill_select_lse(h2o_cache* cache, const void* Q, const void* K
  * 5. The freed slot receives k_new, v_new, pos = t, score = p_new, unless the
  *    new token itself was evicted (then evicted_pos = t and no slot changes
  *    except for the scores of step 3); t_next = t + 1.
+ * A cache stored as codes must have been prefilled first (its key grids come
+ * from the prompt): with t_next == 0 it returns H2O_ESTATE.
+ * Inputs are not scanned for NaN or Inf. A NaN in a head's q or k_new makes
+ * that head's scores and output NaN (one in v_new, its output); its eviction
+ * is still an eligible slot (a NaN score orders above every number and equal
+ * keys fall to the older position), and no other head is affected.
  */
 h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,
                            float* out, int32_t* evicted_pos, h2o_stream_t stream);
@@ -247,7 +259,7 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, c
  * batch x heads heads, head_dim and k = k_heavy + k_recent slots (0 for an
  * invalid shape). The workspace holds the step's logits [batch][heads][k] and
  * up to ceil(k/64) chunk partials per head; it carries nothing from one call
- * to the next.
+ * to the next. Sizing only: no passage on the pages defines this call.
  */
 size_t h2o_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim, int32_t k);
 
@@ -260,7 +272,8 @@ size_t h2o_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim
  * attention"), updates the scores and evicts (H2O §2 "Problem formulation",
  * §D "Cache eviction").
  *   chunk_rows : 0 lets the library choose (about two waves per SIMD in
- *                total); otherwise a positive multiple of 64
+ *                total); otherwise a positive multiple of 64 (a value above
+ *                k rounded up to 64 is taken as that: one chunk per head)
  *   workspace  : device buffer of at least h2o_decode_workspace_bytes(...)
  *                bytes, 256-byte aligned, used only while the call's work
  *                runs on the stream (calls sharing one workspace must be
@@ -272,18 +285,24 @@ h2o_status h2o_decode_step_split(h2o_cache* cache, const void* q, const void* k_
                                  size_t workspace_bytes, h2o_stream_t stream);
 
 /*
- * Export the cache state (checkpoint, inspection). Fills *state from the host
- * counters. If pos_host and/or score_host are non-null ([batch][heads][k]
- * host arrays), the device arrays are copied into them and the call waits for
- * the stream; otherwise it does not touch the device.
+ * Export the cache state (checkpoint, inspection): the fixed-size set of
+ * cached positions and their accumulated scores, S_i and the scores that
+ * drive the next eviction in H2O §2 "Problem formulation" and §D "Cache
+ * eviction". The pages define no checkpoint call; this one is bookkeeping
+ * around that state. Fills *state from the host counters. If pos_host and/or
+ * score_host are non-null ([batch][heads][k] host arrays), the device arrays
+ * are copied into them and the call waits for the stream; otherwise it does
+ * not touch the device.
  */
 h2o_status h2o_cache_state(const h2o_cache* cache, h2o_state* state, int32_t* pos_host,
                            float* score_host, h2o_stream_t stream);
 
 /*
  * Restore the host counter after the caller has written K, V, score and pos
- * back into the device tensors (resume from a checkpoint, or resynchronise
- * from another implementation). Sets t_next and n_used = min(k, t_next).
+ * (and, for a cache of codes, both grids) back into the device tensors:
+ * resume from a checkpoint, or resynchronise from another implementation.
+ * Sets t_next and n_used = min(k, t_next). The counterpart of
+ * h2o_cache_state; no passage on the pages defines it.
  */
 h2o_status h2o_cache_restore(h2o_cache* cache, int32_t t_next, int64_t steps);
 
@@ -297,8 +316,19 @@ h2o_status h2o_fullcache_decode(int32_t batch, int32_t heads, int32_t head_dim, 
                                 float scale, int32_t len, const void* q, const void* Kc,
                                 const void* Vc, float* out, h2o_stream_t stream);
 
-/* Message for the last non-OK status returned on the calling thread. */
+/*
+ * Message for the last non-OK status returned on the calling thread (error
+ * reporting; no passage on the pages defines it).
+ */
 const char* h2o_last_error(void);
+
+/*
+ * 16 hex digits identifying the sources the library was built from (a
+ * SHA-256 prefix over its kernel sources and this header), so that a caller
+ * can refuse a binary older than its sources. Build identification; no
+ * passage on the pages defines it.
+ */
+const char* h2o_build_digest(void);
 
 #ifdef __cplusplus
 }

@@ -78,8 +78,6 @@ _I = ctypes.c_int32
 _SIGNATURES = {
     "h2o_cache_init": (_I, [ctypes.POINTER(h2o_cache), _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                             _P, _P, _P, _P, _P]),
-    "h2o_cache_init_u8": (_I, [ctypes.POINTER(h2o_cache), _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
-                               _P, _P, _P, _P, _P, _P, _P]),
     "h2o_cache_init_quant": (_I, [ctypes.POINTER(h2o_cache), _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                                   _P, _P, _P, _P, _P, _P, _P]),
     "h2o_prefill_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
@@ -95,11 +93,13 @@ _SIGNATURES = {
     "h2o_cache_restore": (_I, [ctypes.POINTER(h2o_cache), _I, ctypes.c_int64]),
     "h2o_fullcache_decode": (_I, [_I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P, _P, _P]),
     "h2o_last_error": (ctypes.c_char_p, []),
+    "h2o_build_digest": (ctypes.c_char_p, []),
 }
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the built HIP library (raises if it has not been built)."""
+    """Load the built HIP library. Raises if it has not been built, or if the
+    in-tree library was built from sources other than the ones beside it."""
     global _lib
     if _lib is not None:
         return _lib
@@ -109,6 +109,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = res, args
+    if os.path.abspath(path) == os.path.abspath(LIB_PATH):
+        from .build import source_digest
+        have, want = lib.h2o_build_digest().decode(), source_digest()
+        if have != want:
+            raise ImportError(f"{path} was built from sources {have}, the sources beside it are {want}: "
+                              "rebuild with `python -m kv_cache_eviction_decode_amd.build`")
     _lib = lib
     return lib
 
@@ -150,6 +156,10 @@ def _expect(t: torch.Tensor, name: str, shape, dtype, device=None):
 # ----------------------------------------------------------------------------- C names
 def h2o_last_error() -> str:
     return load_library().h2o_last_error().decode()
+
+
+def h2o_build_digest() -> str:
+    return load_library().h2o_build_digest().decode()
 
 
 def h2o_prefill_workspace_bytes(batch: int, heads: int, n: int) -> int:
@@ -195,13 +205,6 @@ def h2o_cache_init_quant(desc: h2o_cache, batch, heads, head_dim, k_heavy, k_rec
                                                code, DTYPE_CODE[dtype], float(scale), QUANT_CODE[quant],
                                                _ptr(Kq), _ptr(Vq), _ptr(k_qparam), _ptr(v_qparam), _ptr(score),
                                                _ptr(pos), _stream_handle(stream)))
-
-
-def h2o_cache_init_u8(desc: h2o_cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale,
-                      Kq, Vq, k_qparam, v_qparam, score, pos, stream=None):
-    """h2o_cache_init_quant with 8-bit codes."""
-    h2o_cache_init_quant(desc, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, "u8",
-                         Kq, Vq, k_qparam, v_qparam, score, pos, stream)
 
 
 def _desc_dtype(desc):

@@ -155,6 +155,11 @@ extern "C" {
 
 const char* h2o_last_error(void) { return g_err; }
 
+#ifndef H2O_SOURCE_DIGEST
+#define H2O_SOURCE_DIGEST "unknown"
+#endif
+const char* h2o_build_digest(void) { return H2O_SOURCE_DIGEST; }
+
 h2o_status h2o_cache_init(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
                           int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
                           void* K, void* V, float* score, int32_t* pos, h2o_stream_t stream) {
@@ -173,14 +178,6 @@ h2o_status h2o_cache_init_quant(h2o_cache* cache, int32_t batch, int32_t heads, 
     return fail(H2O_EINVAL, "k_qparam and v_qparam must be 16-byte aligned");
   return init_cache(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, Kq, Vq, score, pos,
                     quant, k_qparam, v_qparam, stream);
-}
-
-h2o_status h2o_cache_init_u8(h2o_cache* cache, int32_t batch, int32_t heads, int32_t head_dim,
-                             int32_t k_heavy, int32_t k_recent, int32_t policy, int32_t dtype, float scale,
-                             uint8_t* Kq, uint8_t* Vq, float* k_qparam, float* v_qparam, float* score,
-                             int32_t* pos, h2o_stream_t stream) {
-  return h2o_cache_init_quant(cache, batch, heads, head_dim, k_heavy, k_recent, policy, dtype, scale, H2O_QUANT_U8,
-                              Kq, Vq, k_qparam, v_qparam, score, pos, stream);
 }
 
 size_t h2o_prefill_workspace_bytes(int32_t batch, int32_t heads, int32_t n) {
@@ -224,6 +221,8 @@ h2o_status h2o_decode_step(h2o_cache* cache, const void* q, const void* k_new, c
   if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) || !aligned(evicted_pos, 4))
     return fail(H2O_EINVAL, "q, k_new, v_new, out must be 16-byte aligned; evicted_pos 4-byte aligned");
   if (cache->t_next == INT32_MAX) return fail(H2O_ESTATE, "position counter exhausted");
+  if (cache->quant != H2O_QUANT_NONE && cache->t_next == 0)
+    return fail(H2O_ESTATE, "a cache stored as codes must be prefilled first: its key grids come from the prompt");
 
   const int32_t k = cache->k_heavy + cache->k_recent;
   h2o::DecodeArgs a{};
@@ -295,6 +294,10 @@ h2o_status h2o_decode_step_split(h2o_cache* cache, const void* q, const void* k_
     L = int(((per + kSplitRows - 1) / kSplitRows) * kSplitRows);
     if (L < kSplitRows) L = kSplitRows;
   }
+  // A chunk longer than the cache is one chunk per head (and keeps the
+  // chunk kernel's LDS, 4 bytes per row, within 32 KiB).
+  const int Lmax = int(split_cmax(k)) * kSplitRows;
+  if (L > Lmax) L = Lmax;
   const int chunks = nu > 0 ? (nu + L - 1) / L : 1;
   if (chunks > split_cmax(k)) return fail(H2O_EINVAL, "chunk_rows %d too small for k = %d", L, k);
 

@@ -32,9 +32,8 @@ def gpu():
 
 @pytest.fixture(scope="session", autouse=True)
 def built_library():
-    """Build the HIP library once if it is not there (it is not committed);
-    an existing build is used as it is."""
-    from kv_cache_eviction_decode_amd import binding
-    if not os.path.exists(binding.LIB_PATH):
-        from kv_cache_eviction_decode_amd.build import build
-        build()
+    """Build the HIP library if it is missing (it is not committed) or was
+    built from other sources than the ones in the tree; a current build is
+    used as it is."""
+    from kv_cache_eviction_decode_amd.build import ensure_built
+    ensure_built(verbose=True)

@@ -76,14 +76,6 @@ def test_init_rejects_bad_arguments_without_launching(args, msg):
     assert d.magic == 0  # descriptor untouched
 
 
-def test_u8_init_rejects_missing_grids():
-    lib = b.load_library()
-    d = b.h2o_cache()
-    st = lib.h2o_cache_init_u8(ctypes.byref(d), 1, 1, 128, 4, 4, 0, 1, 0.1, None, None, None, None, None, None,
-                               None)
-    assert st == b.H2O_EINVAL and "k_qparam" in b.h2o_last_error() and d.magic == 0
-
-
 @pytest.mark.parametrize("quant", [b.H2O_QUANT_U8, b.H2O_QUANT_U4, b.H2O_QUANT_U2])
 def test_quant_init_rejects_missing_grids(quant):
     lib = b.load_library()
