@@ -285,6 +285,25 @@ h2o_status h2o_decode_step_split(h2o_cache* cache, const void* q, const void* k_
                                  size_t workspace_bytes, h2o_stream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * h2o_decode_step_split with the same arguments and results, whose workspace
+ * is instead an array of H2O_SPLIT_SCRATCH_BYTES bytes inside the library,
+ * one per GPU, held until the process ends. Its address is looked up once per
+ * device, by h2o_cache_init (or by this call's first use on a device no cache
+ * was initialised on). A shape whose workspace, h2o_decode_workspace_bytes,
+ * exceeds H2O_SPLIT_SCRATCH_BYTES returns H2O_EWORKSPACE before anything is
+ * launched. The call allocates nothing. Every call on one GPU shares that
+ * GPU's array, so calls whose work can overlap on one GPU (unordered streams,
+ * several threads) race: issue them in order on one stream. Nothing in the
+ * array needs to start at zero (each call writes every entry it reads).
+ */
+#define H2O_SPLIT_SCRATCH_BYTES (16u << 20)
+h2o_status h2o_decode_step_split_noalloc(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                         float* out, int32_t* evicted_pos, int32_t chunk_rows,
+                                         h2o_stream_t stream);
+
+/*
  * Export the cache state (checkpoint, inspection): the fixed-size set of
  * cached positions and their accumulated scores, S_i and the scores that
  * drive the next eviction in H2O §2 "Problem formulation" and §D "Cache

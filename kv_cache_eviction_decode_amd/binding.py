@@ -42,6 +42,7 @@ def _header_int(name: str) -> int:
 
 
 H2O_MAX_SLOTS = _header_int("H2O_MAX_SLOTS")
+H2O_SPLIT_SCRATCH_BYTES = 16 << 20  # checked against include/h2o.h by the CPU tests
 H2O_MAX_PROMPT = _header_int("H2O_MAX_PROMPT")
 
 
@@ -89,6 +90,7 @@ _SIGNATURES = {
     "h2o_decode_step": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _P, _P, _P]),
     "h2o_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "h2o_decode_step_split": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _P, _P, _I, _P, ctypes.c_size_t, _P]),
+    "h2o_decode_step_split_noalloc": (_I, [ctypes.POINTER(h2o_cache), _P, _P, _P, _P, _P, _I, _P]),
     "h2o_cache_state": (_I, [ctypes.POINTER(h2o_cache), ctypes.POINTER(h2o_state), _P, _P, _P]),
     "h2o_cache_restore": (_I, [ctypes.POINTER(h2o_cache), _I, ctypes.c_int64]),
     "h2o_fullcache_decode": (_I, [_I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P, _P, _P]),
@@ -291,6 +293,20 @@ def h2o_decode_step_split(desc: h2o_cache, q, k_new, v_new, out, evicted, worksp
                                                 workspace.numel(), _stream_handle(stream)))
 
 
+def h2o_decode_step_split_noalloc(desc: h2o_cache, q, k_new, v_new, out, evicted, chunk_rows: int = 0,
+                                  stream=None, device=None):
+    """h2o_decode_step_split on the library's own workspace (allocates nothing)."""
+    B, H, d = desc.batch, desc.heads, desc.head_dim
+    dt = _desc_dtype(desc)
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new)):
+        _expect(t, name, (B, H, d), dt, device)
+    _expect(out, "out", (B, H, d), torch.float32, device)
+    _expect(evicted, "evicted", (B, H), torch.int32, device)
+    _check(load_library().h2o_decode_step_split_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                                        _ptr(out), _ptr(evicted), int(chunk_rows),
+                                                        _stream_handle(stream)))
+
+
 def h2o_cache_state(desc: h2o_cache, pos_host=None, score_host=None, stream=None) -> h2o_state:
     st = h2o_state()
     k = desc.k_heavy + desc.k_recent
@@ -429,6 +445,11 @@ class H2OCache:
             evicted = torch.empty(self.batch, self.heads, dtype=torch.int32, device=self.device)
         h2o_decode_step_split(self.desc, q, k_new, v_new, out, evicted, self.split_workspace(), chunk_rows,
                               stream, self.device)
+        return out, evicted
+
+    def decode_step_split_noalloc(self, q, k_new, v_new, out, evicted, chunk_rows=0, stream=None):
+        """Split decode step on the library's own workspace; out and evicted must be given."""
+        h2o_decode_step_split_noalloc(self.desc, q, k_new, v_new, out, evicted, chunk_rows, stream, self.device)
         return out, evicted
 
     def state(self, copy=False, stream=None):

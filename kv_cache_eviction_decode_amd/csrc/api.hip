@@ -92,6 +92,12 @@ h2o_status init_cache(h2o_cache* cache, int32_t batch, int32_t heads, int32_t he
   h2o_status st = device_status(
       h2o::launch_cache_clear(score, pos, count, static_cast<hipStream_t>(stream)), "h2o_cache_init");
   if (st != H2O_OK) return st;
+  // Set-up of h2o_decode_step_split_noalloc on this device: the address of
+  // the library's own workspace, so that the step itself makes no runtime
+  // call that could allocate.
+  void* scratch = nullptr;
+  st = device_status(h2o::split_scratch(&scratch), "h2o_cache_init");
+  if (st != H2O_OK) return st;
   *cache = c;
   return H2O_OK;
 }
@@ -146,6 +152,81 @@ h2o_status prefill(h2o_cache* cache, const void* Q, const void* Kp, const void* 
   const int32_t k = cache->k_heavy + cache->k_recent;
   cache->t_next = n;
   cache->n_used = n < k ? n : k;
+  return H2O_OK;
+}
+
+// The split decode step with its workspace already chosen (the caller's, or
+// the library's own array for h2o_decode_step_split_noalloc).
+h2o_status split_step(h2o_cache* cache, const void* q, const void* k_new, const void* v_new, float* out,
+                      int32_t* evicted_pos, int32_t chunk_rows, void* workspace, size_t workspace_bytes,
+                      h2o_stream_t stream, const char* who) {
+  h2o_status st = check_cache(cache);
+  if (st != H2O_OK) return st;
+  if (!q || !k_new || !v_new || !out || !evicted_pos)
+    return fail(H2O_EINVAL, "q, k_new, v_new, out and evicted_pos must be non-NULL");
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) || !aligned(evicted_pos, 4))
+    return fail(H2O_EINVAL, "q, k_new, v_new, out must be 16-byte aligned; evicted_pos 4-byte aligned");
+  if (cache->quant != H2O_QUANT_NONE) return fail(H2O_EINVAL, "split decode takes caches stored in their dtype only");
+  if (chunk_rows < 0 || chunk_rows % kSplitRows != 0)
+    return fail(H2O_EINVAL, "chunk_rows must be 0 or a positive multiple of %d", kSplitRows);
+  const int32_t k = cache->k_heavy + cache->k_recent;
+  const size_t need = h2o_decode_workspace_bytes(cache->batch, cache->heads, cache->head_dim, k);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(H2O_EWORKSPACE, "split decode needs a 256-byte aligned workspace of %zu bytes", need);
+  if (cache->t_next == INT32_MAX) return fail(H2O_ESTATE, "position counter exhausted");
+
+  const int G = cache->batch * cache->heads;
+  const int nu = cache->n_used;
+  int L = chunk_rows;
+  if (L == 0) {
+    // About two waves per SIMD in total, at least one 64-row chunk each.
+    const int64_t target = int64_t(h2o::cu_count()) * 4 * 2;
+    const int64_t per = (int64_t(G) * nu + target - 1) / target;
+    L = int(((per + kSplitRows - 1) / kSplitRows) * kSplitRows);
+    if (L < kSplitRows) L = kSplitRows;
+  }
+  // A chunk longer than the cache is one chunk per head (and keeps the
+  // chunk kernel's LDS, 4 bytes per row, within 32 KiB).
+  const int Lmax = int(split_cmax(k)) * kSplitRows;
+  if (L > Lmax) L = Lmax;
+  const int chunks = nu > 0 ? (nu + L - 1) / L : 1;
+  if (chunks > split_cmax(k)) return fail(H2O_EINVAL, "chunk_rows %d too small for k = %d", L, k);
+
+  h2o::DecodeArgs a{};
+  a.K = cache->K;
+  a.V = cache->V;
+  a.K_w = cache->K;
+  a.V_w = cache->V;
+  a.score = cache->score;
+  a.pos = cache->pos;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.out = out;
+  a.evicted = evicted_pos;
+  a.k = k;
+  a.n_used = nu;
+  a.t = cache->t_next;
+  a.k_recent = cache->k_recent;
+  a.policy = cache->policy;
+  a.c = cache->scale * h2o::kLog2e;
+  char* ws = static_cast<char*>(workspace);
+  const size_t cmax = split_cmax(k);
+  h2o::SplitArgs w{};
+  w.logit = reinterpret_cast<float*>(ws);
+  ws += align256(size_t(G) * k * sizeof(float));
+  w.part_ml = reinterpret_cast<float*>(ws);
+  ws += align256(size_t(G) * cmax * 2 * sizeof(float));
+  w.part_acc = reinterpret_cast<float*>(ws);
+  w.chunk_len = L;
+  w.chunks = chunks;
+  w.cmax = int(cmax);
+  st = device_status(h2o::launch_decode_split(cache->dtype, cache->head_dim, G, a, w, static_cast<hipStream_t>(stream)),
+                     who);
+  if (st != H2O_OK) return st;
+  cache->t_next += 1;
+  cache->n_used = cache->n_used < k ? cache->n_used + 1 : k;
+  cache->steps += 1;
   return H2O_OK;
 }
 
@@ -269,74 +350,25 @@ size_t h2o_decode_workspace_bytes(int32_t batch, int32_t heads, int32_t head_dim
 h2o_status h2o_decode_step_split(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,
                                  float* out, int32_t* evicted_pos, int32_t chunk_rows, void* workspace,
                                  size_t workspace_bytes, h2o_stream_t stream) {
+  return split_step(cache, q, k_new, v_new, out, evicted_pos, chunk_rows, workspace, workspace_bytes, stream,
+                    "h2o_decode_step_split");
+}
+
+h2o_status h2o_decode_step_split_noalloc(h2o_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                         float* out, int32_t* evicted_pos, int32_t chunk_rows,
+                                         h2o_stream_t stream) {
   h2o_status st = check_cache(cache);
   if (st != H2O_OK) return st;
-  if (!q || !k_new || !v_new || !out || !evicted_pos)
-    return fail(H2O_EINVAL, "q, k_new, v_new, out and evicted_pos must be non-NULL");
-  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) || !aligned(evicted_pos, 4))
-    return fail(H2O_EINVAL, "q, k_new, v_new, out must be 16-byte aligned; evicted_pos 4-byte aligned");
-  if (cache->quant != H2O_QUANT_NONE) return fail(H2O_EINVAL, "split decode takes caches stored in their dtype only");
-  if (chunk_rows < 0 || chunk_rows % kSplitRows != 0)
-    return fail(H2O_EINVAL, "chunk_rows must be 0 or a positive multiple of %d", kSplitRows);
   const int32_t k = cache->k_heavy + cache->k_recent;
   const size_t need = h2o_decode_workspace_bytes(cache->batch, cache->heads, cache->head_dim, k);
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-    return fail(H2O_EWORKSPACE, "split decode needs a 256-byte aligned workspace of %zu bytes", need);
-  if (cache->t_next == INT32_MAX) return fail(H2O_ESTATE, "position counter exhausted");
-
-  const int G = cache->batch * cache->heads;
-  const int nu = cache->n_used;
-  int L = chunk_rows;
-  if (L == 0) {
-    // About two waves per SIMD in total, at least one 64-row chunk each.
-    const int64_t target = int64_t(h2o::cu_count()) * 4 * 2;
-    const int64_t per = (int64_t(G) * nu + target - 1) / target;
-    L = int(((per + kSplitRows - 1) / kSplitRows) * kSplitRows);
-    if (L < kSplitRows) L = kSplitRows;
-  }
-  // A chunk longer than the cache is one chunk per head (and keeps the
-  // chunk kernel's LDS, 4 bytes per row, within 32 KiB).
-  const int Lmax = int(split_cmax(k)) * kSplitRows;
-  if (L > Lmax) L = Lmax;
-  const int chunks = nu > 0 ? (nu + L - 1) / L : 1;
-  if (chunks > split_cmax(k)) return fail(H2O_EINVAL, "chunk_rows %d too small for k = %d", L, k);
-
-  h2o::DecodeArgs a{};
-  a.K = cache->K;
-  a.V = cache->V;
-  a.K_w = cache->K;
-  a.V_w = cache->V;
-  a.score = cache->score;
-  a.pos = cache->pos;
-  a.q = q;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.out = out;
-  a.evicted = evicted_pos;
-  a.k = k;
-  a.n_used = nu;
-  a.t = cache->t_next;
-  a.k_recent = cache->k_recent;
-  a.policy = cache->policy;
-  a.c = cache->scale * h2o::kLog2e;
-  char* ws = static_cast<char*>(workspace);
-  const size_t cmax = split_cmax(k);
-  h2o::SplitArgs w{};
-  w.logit = reinterpret_cast<float*>(ws);
-  ws += align256(size_t(G) * k * sizeof(float));
-  w.part_ml = reinterpret_cast<float*>(ws);
-  ws += align256(size_t(G) * cmax * 2 * sizeof(float));
-  w.part_acc = reinterpret_cast<float*>(ws);
-  w.chunk_len = L;
-  w.chunks = chunks;
-  w.cmax = int(cmax);
-  st = device_status(h2o::launch_decode_split(cache->dtype, cache->head_dim, G, a, w, static_cast<hipStream_t>(stream)),
-                     "h2o_decode_step_split");
+  if (need > H2O_SPLIT_SCRATCH_BYTES)
+    return fail(H2O_EWORKSPACE, "this shape needs %zu bytes of split-decode workspace, above the library's own %u",
+                need, H2O_SPLIT_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = device_status(h2o::split_scratch(&ws), "h2o_decode_step_split_noalloc");
   if (st != H2O_OK) return st;
-  cache->t_next += 1;
-  cache->n_used = cache->n_used < k ? cache->n_used + 1 : k;
-  cache->steps += 1;
-  return H2O_OK;
+  return split_step(cache, q, k_new, v_new, out, evicted_pos, chunk_rows, ws, H2O_SPLIT_SCRATCH_BYTES, stream,
+                    "h2o_decode_step_split_noalloc");
 }
 
 h2o_status h2o_cache_state(const h2o_cache* cache, h2o_state* state, int32_t* pos_host,

@@ -29,11 +29,24 @@
 // for the merge, and the cross-XCD hand-over needs write-through stores or an
 // L2 write-back, whose latency sits on the critical path.
 
+#include <mutex>
+
+#include "../../include/h2o.h"
 #include "h2o_device.h"
 #include "launch.h"
 
 namespace h2o {
 namespace {
+
+// Workspace of h2o_decode_step_split_noalloc: one array per GPU, held for the
+// life of the process. Host code never uses this name as an address (on the
+// host it is only a stand-in for the symbol); it uses the device address
+// that hipGetSymbolAddress returns, kept per device by split_scratch().
+static __device__ __align__(256) char scratch[H2O_SPLIT_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr int kMergeThreads = 256;
 constexpr int kMergeWaves = kMergeThreads / 64;
@@ -345,6 +358,22 @@ hipError_t launch_split_typed(int G, const DecodeArgs& a, const SplitArgs& w, hi
 }
 
 }  // namespace
+
+hipError_t split_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode_split(int dtype, int head_dim, int G, const DecodeArgs& a, const SplitArgs& w,
                                hipStream_t s) {

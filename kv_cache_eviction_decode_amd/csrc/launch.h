@@ -61,6 +61,10 @@ constexpr int kMaxChunks = 128;
 hipError_t launch_decode_split(int dtype, int head_dim, int G, const DecodeArgs& a, const SplitArgs& s,
                                hipStream_t st);
 
+// Device address of the library's own split-decode workspace on the current
+// device (H2O_SPLIT_SCRATCH_BYTES bytes), looked up once per device.
+hipError_t split_scratch(void** ptr);
+
 // Plain attention of one query over a contiguous cache of n_used rows.
 hipError_t launch_fullcache(int dtype, int head_dim, int G, const DecodeArgs& a, hipStream_t s);
 

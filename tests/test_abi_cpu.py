@@ -114,6 +114,27 @@ def test_calls_on_uninitialised_cache_are_rejected():
     assert lib.h2o_decode_step(None, None, None, None, None, None, None) == b.H2O_EINVAL
 
 
+def test_noalloc_split_rejects_before_launching():
+    """The allocation-free split step checks the cache and its workspace need
+    against the library's own array before any device call."""
+    lib = b.load_library()
+    d = b.h2o_cache()
+    assert lib.h2o_decode_step_split_noalloc(ctypes.byref(d), None, None, None, None, None, 0, None) == b.H2O_ESTATE
+    assert lib.h2o_decode_step_split_noalloc(None, None, None, None, None, None, 0, None) == b.H2O_EINVAL
+    # a descriptor as h2o_cache_init would leave it, for 256 heads x 8192 slots: 24 MiB of workspace
+    big = b.h2o_cache(batch=8, heads=32, head_dim=128, k_heavy=4096, k_recent=4096, magic=0x48324F31)
+    need = b.h2o_decode_workspace_bytes(8, 32, 128, 8192)
+    assert need > b.H2O_SPLIT_SCRATCH_BYTES
+    st = lib.h2o_decode_step_split_noalloc(ctypes.byref(big), None, None, None, None, None, 0, None)
+    assert st == b.H2O_EWORKSPACE and str(need) in b.h2o_last_error()
+
+
+def test_scratch_size_matches_header():
+    text = open(b.HEADER).read()
+    m = re.search(r"#define\s+H2O_SPLIT_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == b.H2O_SPLIT_SCRATCH_BYTES
+
+
 def test_fullcache_rejects_bad_arguments():
     lib = b.load_library()
     assert lib.h2o_fullcache_decode(1, 1, 128, 1, 0.1, 0, None, None, None, None, None) == b.H2O_EINVAL
