@@ -74,7 +74,7 @@ import numpy as np
 
 from . import quant as qz
 
-__all__ = ["causal_attention_probs", "prefill_column_sums", "prefill_attention", "select_prefill", "retention_value",
+__all__ = ["causal_attention_probs", "causal_attention_probs_rows", "prefill_column_sums", "prefill_attention", "select_prefill", "retention_value",
            "eligible_slots", "choose_victim", "H2OOracle", "PrefillResult", "StepResult", "POLICIES"]
 
 POLICIES = ("accumulated", "averaged", "position")
@@ -132,15 +132,34 @@ def prefill_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float)
     return (E / Z) @ V, (mx + np.log(Z))[:, 0]
 
 
-def prefill_column_sums(Q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
+def prefill_column_sums(Q: np.ndarray, K: np.ndarray, scale: float, block: int = 1024) -> np.ndarray:
     """c_j: total normalised attention that prompt token j receives from all prompt queries.
 
     This is the accumulated attention statistic of H2O §1 ("Greedy algorithm for
     low-cost policy") and §4.1, taken over the whole prompt (diagonal included).
+    The query rows are taken `block` at a time: each row's softmax is complete
+    within its block (H2O §D "Recursive attention": row i is normalised by its
+    own D_i), so c is the sum of the blocks' column sums and memory stays at
+    block x n values whatever the prompt length.
     """
-    if np.asarray(Q).shape[0] == 0:
-        return np.zeros(0, np.float64)
-    return causal_attention_probs(Q, K, scale).sum(axis=0)
+    Q = np.asarray(Q, np.float64)
+    K = np.asarray(K, np.float64)
+    n = Q.shape[0]
+    c = np.zeros(n, np.float64)
+    for r0 in range(0, n, block):
+        r1 = min(n, r0 + block)
+        c[:r1] += causal_attention_probs_rows(Q[r0:r1], K[:r1], scale, r0).sum(axis=0)
+    return c
+
+
+def causal_attention_probs_rows(Qb: np.ndarray, K: np.ndarray, scale: float, r0: int) -> np.ndarray:
+    """Rows r0 .. r0 + len(Qb) - 1 of the causal attention matrix, over keys 0 .. len(K) - 1
+    (row i attends over keys j <= i, H2O §D "Recursive attention")."""
+    rows = np.arange(r0, r0 + Qb.shape[0])[:, None]
+    S = scale * (Qb @ K.T)
+    S = np.where(np.arange(K.shape[0])[None, :] <= rows, S, -np.inf)
+    E = np.exp(S - S.max(axis=1, keepdims=True))
+    return E / E.sum(axis=1, keepdims=True)
 
 
 def select_prefill(c: np.ndarray, k_heavy: int, k_recent: int, policy: str = "accumulated"):
@@ -194,11 +213,12 @@ def choose_victim(value: np.ndarray, pos: np.ndarray, eligible: np.ndarray, exac
     tied = eligible & (value == smallest[:, None])
     victim = np.argmin(np.where(tied, pos, np.iinfo(np.int64).max), axis=1)
     margin = np.full(G, np.inf)
-    if not exact:
-        for g in range(G):
-            e = np.sort(value[g][eligible[g]])
-            if e.size >= 2:
-                margin[g] = (e[1] - e[0]) / e[1] if e[1] > 0 else 0.0
+    if not exact and value.shape[1] >= 2:
+        e = np.sort(masked, axis=1)  # the eligible values first, ascending
+        e0, e1 = e[:, 0], e[:, 1]
+        two = eligible.sum(axis=1) >= 2
+        gap = np.divide(e1 - e0, e1, out=np.zeros(G), where=two & (e1 > 0))
+        margin = np.where(two, gap, np.inf)
     return victim, margin
 
 
@@ -272,8 +292,11 @@ class H2OOracle:
         self.K[g, slots] = qz.dequantize(kc, self.k_scale[g], self.k_min[g])
         self.V[g, slots] = qz.dequantize(vc, vs[..., None], vm[..., None])
 
-    def prefill(self, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> PrefillResult:
-        """Score the prompt and seed the cache (H2O §A "Pseudocode"); Q, K, V are [G, n, d]."""
+    def prefill(self, Q: np.ndarray, K: np.ndarray, V: np.ndarray, workers: int = 1) -> PrefillResult:
+        """Score the prompt and seed the cache (H2O §A "Pseudocode"); Q, K, V are [G, n, d].
+
+        workers > 1 computes the heads' column sums on that many threads (the
+        heads are independent; each head's arithmetic is unchanged)."""
         Q = np.asarray(Q, np.float64)
         K = np.asarray(K, np.float64)
         V = np.asarray(V, np.float64)
@@ -286,8 +309,15 @@ class H2OOracle:
         self.pos[:] = -1
         self.K[:] = 0.0
         self.V[:] = 0.0
+        if workers > 1 and self.G > 1:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(min(workers, self.G)) as ex:
+                for g, c in enumerate(ex.map(lambda h: prefill_column_sums(Q[h], K[h], self.scale), range(self.G))):
+                    colsum[g] = c
+        else:
+            for g in range(self.G):
+                colsum[g] = prefill_column_sums(Q[g], K[g], self.scale)
         for g in range(self.G):
-            colsum[g] = prefill_column_sums(Q[g], K[g], self.scale)
             keep, margin[g] = select_prefill(colsum[g], self.k_heavy, self.k_recent, self.policy)
             m = keep.size
             self.pos[g, :m] = keep
@@ -313,11 +343,11 @@ class H2OOracle:
         Kc, Vc = self.K[:, :nu], self.V[:, :nu]
 
         logits = np.concatenate(
-            [self.scale * np.einsum("gkd,gd->gk", Kc, q),
-             self.scale * np.einsum("gd,gd->g", k_new, q)[:, None]], axis=1)
+            [self.scale * np.matmul(Kc, q[:, :, None])[:, :, 0],
+             self.scale * (k_new * q).sum(axis=1)[:, None]], axis=1)
         e = np.exp(logits - logits.max(axis=1, keepdims=True))
         p = e / e.sum(axis=1, keepdims=True)
-        out = np.einsum("gk,gkd->gd", p[:, :nu], Vc) + p[:, nu:nu + 1] * v_new
+        out = np.matmul(p[:, None, :nu], Vc)[:, 0, :] + p[:, nu:nu + 1] * v_new
 
         self.score[:, :nu] += p[:, :nu]
 
@@ -342,8 +372,12 @@ class H2OOracle:
 
         ins = slot >= 0
         r, sl = rows[ins], slot[ins]
-        for g, s_ in zip(r, sl):
-            self._store_rows(g, np.array([s_]), k_new[g][None], v_new[g][None])
+        if self.quant:
+            for g, s_ in zip(r, sl):
+                self._store_rows(g, np.array([s_]), k_new[g][None], v_new[g][None])
+        else:
+            self.K[r, sl] = k_new[r]
+            self.V[r, sl] = v_new[r]
         self.pos[r, sl] = self.t
         self.score[r, sl] = p[ins, nu]
         self.t += 1

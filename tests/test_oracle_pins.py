@@ -313,11 +313,17 @@ def _mutant_is_caught(monkeypatch, attr, fake):
 
 def test_planted_mistakes_are_caught(monkeypatch):
     orig_probs = oh.causal_attention_probs
+    orig_rows = oh.causal_attention_probs_rows
     orig_select = oh.select_prefill
+
+    def no_diagonal(Qb, K, s, r0):
+        P = orig_rows(Qb, K, s, r0)
+        P = np.where(np.arange(K.shape[0])[None, :] < np.arange(r0, r0 + Qb.shape[0])[:, None], P, 0.0)
+        return P / np.maximum(P.sum(1, keepdims=True), 1e-300)
+
     mutants = {
         # diagonal dropped from prefill attention
-        "causal_attention_probs": lambda Q, K, s: np.tril(orig_probs(Q, K, s), -1)
-        / np.maximum(np.tril(orig_probs(Q, K, s), -1).sum(1, keepdims=True), 1e-300),
+        "causal_attention_probs_rows": no_diagonal,
         # row sums instead of column sums
         "prefill_column_sums": lambda Q, K, s: orig_probs(Q, K, s).sum(axis=1),
         # recent window off by one
@@ -415,3 +421,29 @@ def test_prefill_attention_is_causal_sdpa():
     O0, lse0 = prefill_attention(np.zeros((n, d)), K, V, scale)
     np.testing.assert_allclose(O0, np.cumsum(V, 0) / np.arange(1, n + 1)[:, None], rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse0, np.log(np.arange(1, n + 1)), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- row blocks
+@pytest.mark.parametrize("block", [1, 7, 64])
+def test_row_blocked_column_sums_equal_whole_matrix(block):
+    """Column sums taken over row blocks equal those of the whole causal
+    attention matrix (each row's softmax is complete within its block)."""
+    rng = np.random.default_rng(block)
+    n, d = 150, 16
+    Q, K = rng.standard_normal((n, d)) + 1.0, rng.standard_normal((n, d))
+    whole = oh.causal_attention_probs(Q, K, 0.3).sum(axis=0)
+    np.testing.assert_allclose(oh.prefill_column_sums(Q, K, 0.3, block=block), whole, rtol=1e-13, atol=1e-15)
+    # all-zero queries: uniform rows, c_j = H_n - H_j, whatever the blocking
+    Hn = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1))])
+    np.testing.assert_allclose(oh.prefill_column_sums(np.zeros((n, d)), K, 0.3, block=block), Hn[n] - Hn[:n],
+                               rtol=1e-13)
+
+
+def test_threaded_prefill_is_bit_identical():
+    rng = np.random.default_rng(5)
+    G, n, d = 6, 90, 8
+    Q, K, V = (rng.standard_normal((G, n, d)) for _ in range(3))
+    a, b = H2OOracle(G, d, 10, 10, 0.35), H2OOracle(G, d, 10, 10, 0.35)
+    ra, rb = a.prefill(Q, K, V), b.prefill(Q, K, V, workers=4)
+    assert np.array_equal(ra.colsum, rb.colsum) and np.array_equal(a.pos, b.pos)
+    assert np.array_equal(a.score, b.score) and np.array_equal(a.K, b.K)
