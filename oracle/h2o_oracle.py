@@ -74,6 +74,28 @@ import numpy as np
 
 from . import quant as qz
 
+
+def _over_heads(G: int, workers: int, fn) -> None:
+    """Call fn(heads) for contiguous head ranges covering range(G), on up to
+    `workers` threads with BLAS single-threaded inside them. Heads are
+    independent, so the results are those of one call over all heads."""
+    if workers <= 1 or G <= 1:
+        fn(slice(0, G))
+        return
+    from concurrent.futures import ThreadPoolExecutor
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1, user_api="blas")
+    except Exception:  # threadpoolctl missing: BLAS keeps its own threads
+        limit = None
+    try:
+        parts = min(workers, G)
+        with ThreadPoolExecutor(parts) as ex:
+            list(ex.map(lambda i: fn(slice(i * G // parts, (i + 1) * G // parts)), range(parts)))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+
 __all__ = ["causal_attention_probs", "causal_attention_probs_rows", "prefill_column_sums", "prefill_attention", "select_prefill", "retention_value",
            "eligible_slots", "choose_victim", "H2OOracle", "PrefillResult", "StepResult", "POLICIES"]
 
@@ -247,7 +269,9 @@ class H2OOracle:
     """
 
     def __init__(self, n_heads: int, head_dim: int, k_heavy: int, k_recent: int, scale: float,
-                 policy: str = "accumulated", quant: str | None = None):
+                 policy: str = "accumulated", quant: str | None = None, workers: int = 1):
+        """workers > 1 evaluates independent heads on that many threads (the
+        per-head arithmetic, and so every result, is unchanged)."""
         if k_heavy < 0 or k_recent < 0 or k_heavy + k_recent < 1:
             raise ValueError("need k_heavy >= 0, k_recent >= 0 and k >= 1")
         if policy not in POLICIES:
@@ -256,6 +280,7 @@ class H2OOracle:
             raise ValueError(f"unknown quantisation {quant!r}")
         self.policy = policy
         self.quant = quant
+        self.workers = max(1, int(workers))
         self.bits = qz.BITS[quant] if quant else None
         self.G, self.d = n_heads, head_dim
         self.k_heavy, self.k_recent = k_heavy, k_recent
@@ -292,11 +317,13 @@ class H2OOracle:
         self.K[g, slots] = qz.dequantize(kc, self.k_scale[g], self.k_min[g])
         self.V[g, slots] = qz.dequantize(vc, vs[..., None], vm[..., None])
 
-    def prefill(self, Q: np.ndarray, K: np.ndarray, V: np.ndarray, workers: int = 1) -> PrefillResult:
+    def prefill(self, Q: np.ndarray, K: np.ndarray, V: np.ndarray, workers: int | None = None) -> PrefillResult:
         """Score the prompt and seed the cache (H2O §A "Pseudocode"); Q, K, V are [G, n, d].
 
-        workers > 1 computes the heads' column sums on that many threads (the
-        heads are independent; each head's arithmetic is unchanged)."""
+        workers (default: the oracle's) > 1 computes the heads' column sums on
+        that many threads (the heads are independent; each head's arithmetic
+        is unchanged)."""
+        workers = self.workers if workers is None else workers
         Q = np.asarray(Q, np.float64)
         K = np.asarray(K, np.float64)
         V = np.asarray(V, np.float64)
@@ -309,14 +336,11 @@ class H2OOracle:
         self.pos[:] = -1
         self.K[:] = 0.0
         self.V[:] = 0.0
-        if workers > 1 and self.G > 1:
-            from concurrent.futures import ThreadPoolExecutor
-            with ThreadPoolExecutor(min(workers, self.G)) as ex:
-                for g, c in enumerate(ex.map(lambda h: prefill_column_sums(Q[h], K[h], self.scale), range(self.G))):
-                    colsum[g] = c
-        else:
-            for g in range(self.G):
+        def column_sums(heads):
+            for g in range(self.G)[heads]:
                 colsum[g] = prefill_column_sums(Q[g], K[g], self.scale)
+
+        _over_heads(self.G, workers if n else 1, column_sums)
         for g in range(self.G):
             keep, margin[g] = select_prefill(colsum[g], self.k_heavy, self.k_recent, self.policy)
             m = keep.size
@@ -342,12 +366,22 @@ class H2OOracle:
         nu, G = self.n_used, self.G
         Kc, Vc = self.K[:, :nu], self.V[:, :nu]
 
-        logits = np.concatenate(
-            [self.scale * np.matmul(Kc, q[:, :, None])[:, :, 0],
-             self.scale * (k_new * q).sum(axis=1)[:, None]], axis=1)
+        qk = np.empty((G, nu))
+
+        def dots(heads):
+            qk[heads] = np.matmul(Kc[heads], q[heads, :, None])[:, :, 0]
+
+        _over_heads(G, self.workers, dots)
+        logits = np.concatenate([self.scale * qk, self.scale * (k_new * q).sum(axis=1)[:, None]], axis=1)
         e = np.exp(logits - logits.max(axis=1, keepdims=True))
         p = e / e.sum(axis=1, keepdims=True)
-        out = np.matmul(p[:, None, :nu], Vc)[:, 0, :] + p[:, nu:nu + 1] * v_new
+        pv = np.empty((G, self.d))
+
+        def weighted(heads):
+            pv[heads] = np.matmul(p[heads, None, :nu], Vc[heads])[:, 0, :]
+
+        _over_heads(G, self.workers, weighted)
+        out = pv + p[:, nu:nu + 1] * v_new
 
         self.score[:, :nu] += p[:, :nu]
 
@@ -391,3 +425,11 @@ class H2OOracle:
             snap.update(Kq=self.Kq.copy(), Vq=self.Vq.copy(), k_scale=self.k_scale.copy(),
                         k_min=self.k_min.copy(), v_scale=self.v_scale.copy(), v_min=self.v_min.copy())
         return snap
+
+    def restore(self, snap: dict) -> None:
+        """Put back a state taken with snapshot() (arrays are copied in)."""
+        for name, value in snap.items():
+            if isinstance(value, np.ndarray):
+                getattr(self, name)[...] = value
+            else:
+                setattr(self, name, value)

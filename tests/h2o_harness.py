@@ -17,8 +17,9 @@ sides take each rounding decision with the same fp32 operations).
 """
 from __future__ import annotations
 
+import os
 import sys
-from dataclasses import dataclass, field
+from dataclasses import asdict, dataclass, field
 
 import numpy as np
 import torch
@@ -49,8 +50,31 @@ def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(arr)).to(device).to(TORCH_DTYPE[dtype])
 
 
+# Near-ties the oracle's margin excuses may not become the norm: at most 1% of
+# the evictions checked (plus one), and at most 1% of the heads' prefill
+# selections (at least 2). Over the full-size workloads the oracle's own
+# eviction margins never fall below 0.2, and about 1% of heads have a
+# selection margin below 1e-5 at the OPT-6.7B shape.
+EXCUSED_EVICTION_FRAC = 0.01
+EXCUSED_SELECTION_FRAC = 0.01
+
+# Every ParityRun's report, for the end-of-session summary (tests/conftest.py).
+REPORTS: list = []
+
+
+def oracle_workers() -> int:
+    """Threads for the oracle: the CPUs this process may use, at most 16."""
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
 @dataclass
 class Report:
+    name: str = ""
+    entry: str = ""
+    heads: int = 0
     steps: int = 0
     max_out_err: float = 0.0
     max_score_rel: float = 0.0
@@ -62,6 +86,16 @@ class Report:
     evictions_checked: int = 0
     notes: list = field(default_factory=list)
 
+    def check_excusals(self):
+        """Excused near-ties stay rare (see EXCUSED_*_FRAC)."""
+        assert self.excused_evictions <= EXCUSED_EVICTION_FRAC * self.evictions_checked + 1, \
+            f"{self.name}: {self.excused_evictions} of {self.evictions_checked} evictions excused"
+        assert self.excused_selections <= max(2, EXCUSED_SELECTION_FRAC * self.heads), \
+            f"{self.name}: {self.excused_selections} of {self.heads} selections excused"
+
+    def as_dict(self) -> dict:
+        return asdict(self)
+
 
 def _rel_err(got, ref):
     return np.abs(got - ref) / np.maximum(np.abs(ref), SCORE_ATOL / SCORE_RTOL)
@@ -69,7 +103,7 @@ def _rel_err(got, ref):
 
 class ParityRun:
     def __init__(self, wl: Workload, steps: int, sample=None, device="cuda", seed=None, policy="accumulated",
-                 split_rows=None, quant=None):
+                 split_rows=None, quant=None, label=None):
         """split_rows: None decodes with h2o_decode_step; an int (0 = the library's
         choice) decodes with h2o_decode_step_split in chunks of that many rows."""
         self.wl = wl
@@ -100,8 +134,13 @@ class ParityRun:
         self.quant = quant
         self.cache = H2OCache(B, H, d, wl.k_heavy, wl.k_recent, TORCH_DTYPE[wl.dtype], wl.scale, dev,
                               policy=policy, quant=quant)
-        self.orc = H2OOracle(self.sample.size, d, wl.k_heavy, wl.k_recent, wl.scale, policy, quant=quant)
-        self.report = Report()
+        self.orc = H2OOracle(self.sample.size, d, wl.k_heavy, wl.k_recent, wl.scale, policy, quant=quant,
+                             workers=oracle_workers())
+        self.report = Report(name=label or wl.name, entry=mode + (f" {quant}" if quant else ""),
+                             heads=int(self.sample.size))
+        if label:  # labelled runs (the full-size workloads) are listed in the session summary
+            REPORTS.append(self.report)
+        self.prefill_state = None  # oracle state and result right after prefill (see prefill(reuse=...))
 
     # -- views of the sampled heads on the GPU
     def _gpu_sampled(self, t: torch.Tensor) -> np.ndarray:
@@ -145,10 +184,12 @@ class ParityRun:
             "value grids differ"
 
     # -- prefill
-    def prefill(self, check_rows=True, mode="select"):
+    def prefill(self, check_rows=True, mode="select", reuse=None):
         """mode: "select" (h2o_prefill_select), "attention" (h2o_prefill_attention,
         whose prompt output and log normalisers are checked too) or "lse"
-        (h2o_prefill_select_lse fed with the oracle's normalisers)."""
+        (h2o_prefill_select_lse fed with the oracle's normalisers).
+        reuse: another run's prefill_state on the same workload and sample,
+        restored instead of running the oracle's prefill again."""
         wl, rep = self.wl, self.report
         n = wl.prompt_len
         colsum = torch.empty(wl.batch, wl.heads, n, dtype=torch.float32, device=self.device) if n else None
@@ -167,7 +208,12 @@ class ParityRun:
             self.cache.prefill_select_lse(self.Q, self.K, self.V, lse, colsum_out=colsum)
         else:
             self.cache.prefill_select(self.Q, self.K, self.V, colsum_out=colsum)
-        pre = self.orc.prefill(self.oQ, self.oK, self.oV)
+        if reuse is not None:
+            snap, pre = reuse
+            self.orc.restore(snap)
+        else:
+            pre = self.orc.prefill(self.oQ, self.oK, self.oV)
+        self.prefill_state = (self.orc.snapshot(), pre)
         torch.cuda.synchronize()
         if mode == "attention" and n:
             gout = self._gpu_sampled(out)
@@ -188,15 +234,14 @@ class ParityRun:
             rel = _rel_err(gcol, pre.colsum)
             rep.max_colsum_rel = float(rel.max())
             assert rel.max() <= SCORE_RTOL, f"colsum rel err {rel.max():.3g}"
-        for g in range(self.sample.size):
-            if np.array_equal(gpos[g], self.orc.pos[g]):
-                continue
+        for g in np.nonzero((gpos != self.orc.pos).any(axis=1))[0]:
             # near-tie at the selection boundary: either set is correct
             assert pre.margin[g] < MARGIN, f"head {self.sample[g]}: selection differs, margin {pre.margin[g]:.3g}"
             self._check_valid_selection(gpos[g], pre.colsum[g])
             rep.excused_selections += 1
-            differ.append(g)
-        same = np.array([g not in differ for g in range(self.sample.size)])
+            differ.append(int(g))
+        same = np.ones(self.sample.size, bool)
+        same[differ] = False
         if same.any():
             np.testing.assert_array_less(_rel_err(gscore[same], self.orc.score[same]), SCORE_RTOL * (1 + 1e-9))
         if self.quant:
@@ -222,17 +267,22 @@ class ParityRun:
         assert lo_kept >= hi_dropped * (1 - MARGIN), "GPU selection is not a near-tie alternative"
 
     def _check_rows(self, gpos):
-        """Cache rows must be bit-exact copies of the prompt rows they hold."""
+        """Cache rows of every sampled head must be bit-exact copies of the
+        prompt rows they hold (compared on the device, 256 heads at a time)."""
         flatK = self.cache.K.view(self.wl.n_heads_total, self.wl.k, -1)
         flatV = self.cache.V.view(self.wl.n_heads_total, self.wl.k, -1)
         pK = self.K.view(self.wl.n_heads_total, self.wl.prompt_len, -1)
         pV = self.V.view(self.wl.n_heads_total, self.wl.prompt_len, -1)
-        for g, h in enumerate(self.sample[:16]):
-            live = np.nonzero(gpos[g] >= 0)[0]
-            src = torch.from_numpy(gpos[g][live].astype(np.int64)).to(self.device)
-            dst = torch.from_numpy(live.astype(np.int64)).to(self.device)
-            assert torch.equal(flatK[h].index_select(0, dst), pK[h].index_select(0, src))
-            assert torch.equal(flatV[h].index_select(0, dst), pV[h].index_select(0, src))
+        for c0 in range(0, self.sample.size, 256):
+            heads = torch.from_numpy(self.sample[c0:c0 + 256].astype(np.int64)).to(self.device)
+            pos = torch.from_numpy(gpos[c0:c0 + 256].astype(np.int64)).to(self.device)
+            live = pos >= 0
+            src = pos.clamp(min=0)
+            for cache_rows, prompt_rows in ((flatK, pK), (flatV, pV)):
+                got = cache_rows.index_select(0, heads)
+                want = prompt_rows.index_select(0, heads).gather(
+                    1, src[:, :, None].expand(-1, -1, prompt_rows.shape[2]))
+                assert torch.equal(got[live], want[live]), "cache rows differ from the prompt rows they hold"
 
     # -- decode
     def decode(self, steps=None):
@@ -258,17 +308,16 @@ class ParityRun:
             rep.max_out_err = max(rep.max_out_err, err)
             assert err <= tol, f"step {t}: out max abs err {err:.3g} > {tol}"
             differ = []
-            for g in range(self.sample.size):
-                rep.evictions_checked += int(st.evicted[g] >= 0)
-                if gev[g] == st.evicted[g]:
-                    continue
+            rep.evictions_checked += int((st.evicted >= 0).sum())
+            for g in np.nonzero(gev != st.evicted)[0]:
                 assert st.margin[g] < MARGIN, (
                     f"step {t} head {self.sample[g]}: evicted {gev[g]} vs oracle {st.evicted[g]}, "
                     f"margin {st.margin[g]:.3g}")
                 self._check_valid_eviction(g, gev[g], pos_before[g], score_before[g], st, tpos)
                 rep.excused_evictions += 1
-                differ.append(g)
-            same = np.array([g not in differ for g in range(self.sample.size)])
+                differ.append(int(g))
+            same = np.ones(self.sample.size, bool)
+            same[differ] = False
             if same.any():
                 assert np.array_equal(gpos[same], self.orc.pos[same]), f"step {t}: pos differs"
                 rel = _rel_err(gscore[same], self.orc.score[same])
@@ -277,6 +326,7 @@ class ParityRun:
                 self._check_codes(same)
             self.resync(differ)
             rep.steps += 1
+        rep.check_excusals()
         return rep
 
     def _check_valid_eviction(self, g, gpu_evicted, pos_before, score_before, st, tpos):

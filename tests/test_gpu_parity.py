@@ -3,8 +3,11 @@
 Small cases run the oracle on every head; they span several prefill tiles,
 ragged tails, empty and tiny prompts, prompts shorter than the cache,
 k_heavy = 0, the largest k, every dtype and both head sizes. The named
-workloads run at their full shapes (same grid as the benchmark) with the
-oracle following a seeded sample of heads.
+workloads run at their full shapes (same grid as the benchmark) over every
+decode step: every head of the OPT-6.7B, OPT-30B and long-context layers
+(the last with the fused and with the split entry point), and 512 of the
+large-batch layer's 8192 heads, whose every head is also checked over the
+first four steps.
 """
 import zlib
 
@@ -78,7 +81,8 @@ def test_policy_full_size_sampled(gpu):
     """The averaged and heavy-only variants at the OPT-6.7B layer shape (same grid as the bench)."""
     for policy, kh, kr in (("averaged", 128, 128), ("accumulated", 256, 0)):
         wl = WORKLOADS["opt6.7b_layer"].with_(k_heavy=kh, k_recent=kr)
-        run = ParityRun(wl, 48, sample=sample_heads(wl, 16), policy=policy)
+        run = ParityRun(wl, 48, sample=sample_heads(wl, 16), policy=policy,
+                        label=f"opt6.7b_layer {policy} kh={kh} kr={kr} 16 heads x 48 steps")
         run.prefill()
         rep = run.decode()
         log(f"[parity] opt6.7b_layer {policy} k_heavy={kh} k_recent={kr}: {rep}")
@@ -112,18 +116,50 @@ def test_wave_kernel_beyond_prefetch(gpu):
     assert rep.steps == wl.steps
 
 
-FULL = [("opt6.7b_layer", 512, 32), ("opt30b_layer", 64, 16),
-        ("long_context", 24, 4), ("large_batch_f16", 48, 16)]
+# Full-size workloads at the benchmark's grid, over every decode step: every
+# head of the OPT-6.7B and OPT-30B layers, and a seeded sample of 512 of the
+# large-batch layer's 8192 heads (whose every head is checked over the first
+# four steps below).
+EVERY_STEP = [("opt6.7b_layer", None), ("opt30b_layer", None), ("large_batch_f16", 512)]
 
 
-@pytest.mark.parametrize("name,steps,nsample", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled_parity(gpu, name, steps, nsample):
+@pytest.mark.parametrize("name,nsample", EVERY_STEP, ids=[f[0] for f in EVERY_STEP])
+def test_full_size_every_step(gpu, name, nsample):
     wl = WORKLOADS[name]
-    run = ParityRun(wl, steps, sample=sample_heads(wl, nsample))
+    sample = None if nsample is None else sample_heads(wl, nsample)
+    heads = wl.n_heads_total if sample is None else nsample
+    run = ParityRun(wl, wl.steps, sample=sample, label=f"{name} {heads} heads x all steps")
     run.prefill()
     rep = run.decode()
-    log(f"[parity] {name} full size: {rep}")
-    assert rep.steps == steps
+    log(f"[parity] {name} full size, every step: {rep}")
+    assert rep.steps == wl.steps
+
+
+def test_large_batch_all_heads_first_steps(gpu):
+    wl = WORKLOADS["large_batch_f16"]
+    run = ParityRun(wl, 4, label="large_batch_f16 all heads x 4 steps")
+    run.prefill()
+    rep = run.decode()
+    log(f"[parity] large_batch_f16 full size, all heads: {rep}")
+    assert rep.heads == wl.n_heads_total and rep.steps == 4
+
+
+def test_long_context_every_step_fused_and_split(gpu):
+    """The long-context layer (256 heads x 2048 slots, prompt 16384): every
+    head over all 256 steps with the fused step, then again with the split
+    step (the library's chunking), both from the same oracle prefill."""
+    wl = WORKLOADS["long_context"]
+    fused = ParityRun(wl, wl.steps, label="long_context all heads x all steps")
+    fused.prefill()
+    state = fused.prefill_state
+    rep = fused.decode()
+    log(f"[parity] long_context fused, every step: {rep}")
+    del fused
+    split = ParityRun(wl, wl.steps, split_rows=0, label="long_context all heads x all steps")
+    split.prefill(reuse=state)
+    rep_s = split.decode()
+    log(f"[parity] long_context split, every step: {rep_s}")
+    assert rep.steps == rep_s.steps == wl.steps and rep.heads == wl.n_heads_total
 
 
 def test_uniform_attention_closed_form_full_shape(gpu):

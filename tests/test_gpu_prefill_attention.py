@@ -54,7 +54,7 @@ def test_prefill_attention_u8_cache(gpu):
 @pytest.mark.parametrize("name,nsample", [("opt6.7b_layer", 8), ("opt30b_layer", 4), ("long_context", 2)])
 def test_prefill_attention_full_size(gpu, name, nsample):
     wl = WORKLOADS[name]
-    run = ParityRun(wl, 8, sample=sample_heads(wl, nsample))
+    run = ParityRun(wl, 8, sample=sample_heads(wl, nsample), label=f"{name} {nsample} heads, attention prefill")
     run.prefill(mode="attention")
     rep = run.decode()
     log(f"[prefill attention] {name} full size: {rep}")

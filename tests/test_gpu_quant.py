@@ -51,13 +51,15 @@ def test_quant_parity(gpu, case, quant):
 
 @pytest.mark.parametrize("quant", FORMATS)
 def test_quant_opt_layer_full_size(gpu, quant):
-    """The OPT-6.7B layer shape (2048 heads x 256 slots), as in the benchmark."""
+    """The OPT-6.7B layer shape (2048 heads x 256 slots), as in the benchmark:
+    32 heads over all 512 decode steps."""
     wl = WORKLOADS["opt6.7b_layer"]
-    run = ParityRun(wl, 64, sample=sample_heads(wl, 16), quant=quant)
+    run = ParityRun(wl, wl.steps, sample=sample_heads(wl, 32), quant=quant,
+                    label=f"opt6.7b_layer 32 heads x all steps")
     run.prefill()
     rep = run.decode()
     log(f"[{quant}] opt6.7b_layer full size: {rep}")
-    assert rep.steps == 64
+    assert rep.steps == wl.steps
 
 
 @pytest.mark.parametrize("quant", FORMATS)

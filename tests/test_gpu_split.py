@@ -4,9 +4,9 @@ the fp64 oracle, through the C ABI.
 Chunk lengths are chosen so that heads have one chunk, a few, a ragged last
 chunk, more than 64 chunks (the merge loops over lane-sized groups of
 partials) and an empty chunk (empty cache). The cache grows through chunk
-boundaries while it fills. The named long-context workload runs at its full
-shape with the library's own chunking, as in the benchmark, and so does a
-few-heads shape (one sequence of eight heads).
+boundaries while it fills. A few-heads shape (one sequence of eight heads) runs with
+the library's own chunking, as in the benchmark; the long-context workload
+at full size, over every decode step, is in tests/test_gpu_parity.py.
 """
 import zlib
 
@@ -41,16 +41,6 @@ def test_split_parity(gpu, case):
     rep = run.decode()
     log(f"[split] {name} ({policy}, chunk_rows={rows}): {rep}")
     assert rep.steps == T
-
-
-def test_split_long_context_full_size(gpu):
-    """The long-context layer (256 heads x 2048 slots) with the library's chunking."""
-    wl = WORKLOADS["long_context"]
-    run = ParityRun(wl, 24, sample=sample_heads(wl, 4), split_rows=0)
-    run.prefill()
-    rep = run.decode()
-    log(f"[split] long_context full size: {rep}")
-    assert rep.steps == 24
 
 
 def test_split_few_heads_auto_chunks(gpu):

@@ -439,11 +439,32 @@ def test_row_blocked_column_sums_equal_whole_matrix(block):
                                rtol=1e-13)
 
 
-def test_threaded_prefill_is_bit_identical():
+def test_threaded_oracle_is_bit_identical():
     rng = np.random.default_rng(5)
     G, n, d = 6, 90, 8
     Q, K, V = (rng.standard_normal((G, n, d)) for _ in range(3))
-    a, b = H2OOracle(G, d, 10, 10, 0.35), H2OOracle(G, d, 10, 10, 0.35)
-    ra, rb = a.prefill(Q, K, V), b.prefill(Q, K, V, workers=4)
+    q, k, v = (rng.standard_normal((G, 40, d)) for _ in range(3))
+    a, b = H2OOracle(G, d, 10, 10, 0.35), H2OOracle(G, d, 10, 10, 0.35, workers=4)
+    ra, rb = a.prefill(Q, K, V), b.prefill(Q, K, V)
     assert np.array_equal(ra.colsum, rb.colsum) and np.array_equal(a.pos, b.pos)
     assert np.array_equal(a.score, b.score) and np.array_equal(a.K, b.K)
+    for t in range(40):
+        sa, sb = a.decode_step(q[:, t], k[:, t], v[:, t]), b.decode_step(q[:, t], k[:, t], v[:, t])
+        assert np.array_equal(sa.out, sb.out) and np.array_equal(sa.evicted, sb.evicted)
+        assert np.array_equal(a.score, b.score) and np.array_equal(a.pos, b.pos)
+
+
+def test_snapshot_restore_round_trip():
+    rng = np.random.default_rng(9)
+    G, n, d = 3, 40, 8
+    Q, K, V = (rng.standard_normal((G, n, d)) for _ in range(3))
+    q, k, v = (rng.standard_normal((G, 6, d)) for _ in range(3))
+    a = H2OOracle(G, d, 8, 8, 0.35)
+    a.prefill(Q, K, V)
+    snap = a.snapshot()
+    first = [a.decode_step(q[:, t], k[:, t], v[:, t]).evicted for t in range(6)]
+    b = H2OOracle(G, d, 8, 8, 0.35)
+    b.restore(snap)
+    again = [b.decode_step(q[:, t], k[:, t], v[:, t]).evicted for t in range(6)]
+    assert all(np.array_equal(x, y) for x, y in zip(first, again))
+    assert np.array_equal(a.score, b.score) and np.array_equal(a.K, b.K) and a.t == b.t
