@@ -47,7 +47,7 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
-    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="opt6.7b_layer")
     p.add_argument("--layers", type=int, default=4, help="independent layer caches decoded in rotation")
     p.add_argument("--decode-steps", type=int, default=None,
@@ -130,27 +130,32 @@ def load_traffic(workload: str, digest: str, mode: str = "fused"):
 
 def cpu_sample_heads(wl, seconds: float = 15.0) -> int:
     """Heads whose oracle prefill and decode take about `seconds` on 16 host
-    threads (per-head cost measured on the OPT-6.7B layer: 46 ps per n^2 d of
-    prefill, 0.55 ns per step x slot x channel of decode)."""
-    per_head = 4.6e-11 * wl.prompt_len ** 2 * wl.head_dim + 5.5e-10 * wl.steps * wl.k * wl.head_dim
+    threads (per-head cost measured on the OPT-6.7B layer with the oracle's
+    heads on 16 threads: 7.3 ps per n^2 d of prefill, 0.30 ns per step x slot
+    x channel of decode)."""
+    per_head = 7.3e-12 * wl.prompt_len ** 2 * wl.head_dim + 3.0e-10 * wl.steps * wl.k * wl.head_dim
     return int(max(1, min(wl.n_heads_total, round(seconds / per_head))))
 
 
 def cpu_baseline(wl, heads: int, policy: str = "accumulated"):
-    """The fp64 oracle on a bounded sample: `heads` heads, prefill plus every decode step."""
+    """The fp64 oracle on a bounded sample: `heads` heads, prefill plus every decode step.
+
+    The oracle runs as it stands, evaluating independent heads on one thread
+    per CPU this process may use (BLAS single-threaded inside them)."""
     import numpy as np
     from oracle import H2OOracle
     from workload import make_decode, make_prompt, sample_heads
 
+    cores = len(os.sched_getaffinity(0))
     sample = sample_heads(wl, heads or cpu_sample_heads(wl), seed=11)
     Q, K, V = make_prompt(wl, heads=sample)
     q, k, v = make_decode(wl, heads=sample)
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
-    orc = H2OOracle(sample.size, wl.head_dim, wl.k_heavy, wl.k_recent, wl.scale, policy)
+        blas_threads = None
+    orc = H2OOracle(sample.size, wl.head_dim, wl.k_heavy, wl.k_recent, wl.scale, policy, workers=cores)
     t0 = time.perf_counter()
     orc.prefill(Q, K, V)
     t1 = time.perf_counter()
@@ -161,10 +166,14 @@ def cpu_baseline(wl, heads: int, policy: str = "accumulated"):
     return {
         "value": sample.size * wl.steps / (t2 - t0),
         "unit": "head-steps/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
         "sample": (f"{sample.size} of {wl.n_heads_total} heads, full prompt {wl.prompt_len} prefill + "
-                   f"{wl.steps} decode steps, fp64 numpy (prefill {t1 - t0:.2f} s, decode {t2 - t1:.2f} s)"),
+                   f"{wl.steps} decode steps, fp64 numpy on {cores} threads over heads "
+                   f"(prefill {t1 - t0:.2f} s, decode {t2 - t1:.2f} s)"),
+        "decode_only_head_steps_per_s": sample.size * wl.steps / (t2 - t1),
+        "prefill_only_heads_per_s": sample.size / (t1 - t0),
+        "blas_threads": blas_threads,
     }
 
 
@@ -338,7 +347,9 @@ def main():
     step_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
     prefill_ms = [starts[s].elapsed_time(mids[s]) for s in range(args.steps)]
     decode_ms = [mids[s].elapsed_time(ends[s]) for s in range(args.steps)]
-    ms_per_step = sum(step_ms) / args.steps
+    # Every figure is the median over the timed steps (the mean is reported beside it).
+    median = lambda xs: float(np.median(np.asarray(xs, dtype=np.float64)))
+    ms_per_step = median(step_ms)
     head_steps = G * T * L
     value = head_steps / (ms_per_step / 1e3)
 
@@ -349,7 +360,7 @@ def main():
     else:
         bytes_per_launch = G * sum(decode_bytes_per_head(u, d, e) for u in n_used) / T
     launches = T * L
-    avg_launch_s = (sum(decode_ms) / args.steps) / 1e3 / launches
+    avg_launch_s = median(decode_ms) / 1e3 / launches
     achieved = bytes_per_launch / avg_launch_s / 1e9
     mode = args.quant if quant else args.decode
     # the library runs one wave per head when the heads fill half the resident waves (2 per SIMD)
@@ -360,7 +371,7 @@ def main():
     traffic = load_traffic(wl.name, digest, mode) if default_shape else None
     # two causal QK^T passes per layer (d n (n+1) flops each), plus the causal P.V with the output
     prefill_flops = (3.0 if attn else 2.0) * n * (n + 1) * d * G
-    pf_s = (sum(prefill_ms) / args.steps) / 1e3 / L
+    pf_s = median(prefill_ms) / 1e3 / L
 
     single = None
     if not args.no_single_layer and L > 1:
@@ -437,6 +448,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_mean": sum(step_ms) / args.steps,
+        "timing": f"median of {args.steps} timed steps after {args.warmup} warm-up steps (HIP events)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -457,7 +470,7 @@ def main():
                      "library_digest": lib.h2o_build_digest().decode(),
                      "copy_GBps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
                      "copy_note": "plain 1 GiB device-to-device copy (read + write bytes), 5 timed"},
-        "decode_head_steps_per_s": head_steps / (sum(decode_ms) / args.steps / 1e3),
+        "decode_head_steps_per_s": head_steps / (median(decode_ms) / 1e3),
         "prefill": {"ms_per_layer": pf_s * 1e3, "algorithmic_TFLOPs": prefill_flops / pf_s / 1e12,
                     "mfma_frac": prefill_flops / pf_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                     # one causal QK^T pass is the least any exact column sum needs
