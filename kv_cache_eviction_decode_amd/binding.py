@@ -19,7 +19,9 @@ import re
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libh2o.so")
+# The in-tree build; H2O_LIBRARY may name another build of the same sources
+# (e.g. one with the host code sanitised), which is checked the same way.
+LIB_PATH = os.environ.get("H2O_LIBRARY") or os.path.join(PKG, "libh2o.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "h2o.h")
 
 H2O_OK, H2O_EINVAL, H2O_ESTATE, H2O_EWORKSPACE, H2O_EDEVICE = 0, 1, 2, 3, 4
