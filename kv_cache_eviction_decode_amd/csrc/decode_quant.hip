@@ -88,6 +88,28 @@ __global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G
       ks4[i] = kg4[i];
       km4[i] = kg4[D / 4 + i];
     }
+    // The head's first batch of codes goes out right behind its inputs, so
+    // that its latency overlaps the folding of q and the quantisation below.
+    const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * RB + sub * CB;
+    const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * RB + sub * CB;
+    const float2* vg = reinterpret_cast<const float2*>(a.v_qparam) + hrow;
+    // Loads are unconditional (clamped to the last occupied row, masked; slot
+    // 0 when the cache is empty, whose values are then never used) so that
+    // the compiler's wait counts stay exact: a conditional first batch makes
+    // it wait for every load before the quantisation below.
+    const int last = max(nu - 1, 0);
+    auto issue = [&](CT (&kb)[UB], CT (&vb)[UB], float2 (&gb)[UB], int b) {
+#pragma unroll
+      for (int j = 0; j < UB; ++j) {
+        const int row = min((b * UB + j) * RPU + grp, last);
+        kb[j] = LC::load(Kh + size_t(row) * RB);
+        vb[j] = LC::load(Vh + size_t(row) * RB);
+        gb[j] = vg[row];
+      }
+    };
+    CT kA[UB], vA[UB], kB[UB], vB[UB];
+    float2 gA[UB], gB[UB];
+    issue(kA, vA, gA, 0);
     const float* ks = reinterpret_cast<const float*>(ks4);
     const float* km = reinterpret_cast<const float*>(km4);
     float qs[16];
@@ -145,24 +167,10 @@ __global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G
     }
 
     // ---- stream the codes: per lane-group online softmax -------------------------------
-    const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * RB + sub * CB;
-    const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * RB + sub * CB;
-    const float2* vg = reinterpret_cast<const float2*>(a.v_qparam) + hrow;
     float m = kNegInf, l = 0.f, pm = 0.f;  // pm: sum of p * value-grid minimum
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    // Loads are unconditional (clamped to the last occupied row, masked) so
-    // that the compiler's wait counts stay exact.
-    auto issue = [&](CT (&kb)[UB], CT (&vb)[UB], float2 (&gb)[UB], int b) {
-#pragma unroll
-      for (int j = 0; j < UB; ++j) {
-        const int row = min((b * UB + j) * RPU + grp, nu - 1);
-        kb[j] = LC::load(Kh + size_t(row) * RB);
-        vb[j] = LC::load(Vh + size_t(row) * RB);
-        gb[j] = vg[row];
-      }
-    };
     auto compute = [&](const CT (&kb)[UB], const CT (&vb)[UB], const float2 (&gb)[UB], int b) {
       float s[UB];
       float bm = kNegInf;
@@ -204,9 +212,6 @@ __global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G
       }
     };
     if (nb > 0) {
-      CT kA[UB], vA[UB], kB[UB], vB[UB];
-      float2 gA[UB], gB[UB];
-      issue(kA, vA, gA, 0);
       for (int b = 0; b < nb; b += 2) {
         set_wave_priority(3 - (4 * b) / nb);  // lagging waves of a SIMD issue first
         issue(kB, vB, gB, b + 1);

@@ -163,6 +163,10 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
   const auto Kr = T::rows(Kh, n);
   const float c = a.c;
 
+  // The first key tile is fetched together with the query fragments, so the
+  // prologue waits for one memory latency, not two.
+  uint4 nx[T::CPT];
+  T::fetch(nx, Kr, 0);
   uint4 qf[2][T::KS];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -174,8 +178,6 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
   float ref[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
   const int ntiles = min(wg_q0 + QBLK - 1, n - 1) / 64 + 1;
   const int nfull = min(wg_q0 / 64, ntiles);  // tiles with every key <= the workgroup's first query
-  uint4 nx[T::CPT];
-  T::fetch(nx, Kr, 0);
   T::store(lds[0], nx);
   __syncthreads();
 
@@ -359,6 +361,11 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
   const auto Vr = T::rows(Vh, n);
   const float c = a.c;
 
+  // The first key and value tiles are fetched together with the query
+  // fragments (one memory latency in the prologue, not two).
+  uint4 nk[T::CPT], nv[T::CPT];
+  T::fetch(nk, Kr, 0);
+  T::fetch(nv, Vr, 0);
   uint4 qf[T::KS];
   {
     const int r = min(q0 + (lane & 31), n - 1);
@@ -371,9 +378,6 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   float ref = kNegInf, l = 0.f;
   const int ntiles = min(wg_q0 + 255, n - 1) / 64 + 1;
-  uint4 nk[T::CPT], nv[T::CPT];
-  T::fetch(nk, Kr, 0);
-  T::fetch(nv, Vr, 0);
   T::store(lds_k[0], nk);
   VT::store(lds_v[0], nv);
   __syncthreads();
@@ -513,15 +517,6 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
   const float* lse = a.lse2 + size_t(head) * ld_lse;
   const float c = a.c;
 
-  uint4 kf[2][T::KS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int r = min(k0 + kb * 32 + (lane & 31), n - 1);
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) kf[kb][ks] = ld16(Kh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
-  }
-  wait_vmem_all();
-  float sum[2] = {0.f, 0.f}, comp[2] = {0.f, 0.f};
   const int t0 = wg_k0 / 64;
   const int ntiles = (n + 63) / 64;
   uint4 nx[T::CPT];
@@ -539,7 +534,18 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
     T::store(lds[buf], nx);
     if (threadIdx.x < 64) lds_lse[buf][threadIdx.x] = nl;
   };
+  // The first query tile is fetched together with the key fragments, so the
+  // prologue waits for one memory latency, not two.
   fetch(t0);
+  uint4 kf[2][T::KS];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = min(k0 + kb * 32 + (lane & 31), n - 1);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) kf[kb][ks] = ld16(Kh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
+  }
+  wait_vmem_all();
+  float sum[2] = {0.f, 0.f}, comp[2] = {0.f, 0.f};
   store(0);
   __syncthreads();
   auto step = [&](int qt, auto masked) {
