@@ -625,60 +625,215 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
 }
 
 // ---------------------------------------------------------------- fp32 (VALU)
-// fp32 inputs have no dense MFMA rate worth using at these sizes; one thread
-// per query (pass 1) or per key (pass 2).
+// fp32 operands run on the vector ALU. A workgroup of 256 lanes owns 64 rows of
+// one head (queries in the row passes, keys in the column pass): the four lanes
+// of a quad share a row, lane s holding float4 columns s, s+4, s+8, ... of it in
+// registers. The other operand streams through LDS 32 rows at a time, fetched
+// into registers one tile ahead. For a group of four streamed rows, lane s
+// forms the partial dot product of its columns with row (r ^ s) as its r-th
+// value; two quad swaps then leave lane s holding the full score against row s
+// of the group, so every score is finished in exactly one lane and the softmax
+// arithmetic is not repeated across the quad.
+constexpr int kF32Threads = 256;
+constexpr int kF32Rows = kF32Threads / 4;  // rows owned by a workgroup
+constexpr int kF32Tile = 32;               // streamed rows per LDS tile
+
+template <int D> struct F32Layout {
+  static constexpr int C4 = D / 16;                   // float4 columns per lane
+  static constexpr int TILE4 = kF32Tile * D / 4;      // float4 per LDS tile
+  static constexpr int LOADS = TILE4 / kF32Threads;   // float4 per lane per tile
+  static_assert(TILE4 % kF32Threads == 0, "tile must split evenly over the workgroup");
+};
+
+// One lane's columns of row r of a [n][D] matrix (zeros past n).
 template <int D>
-__global__ __launch_bounds__(256) void rowlse_valu(PrefillArgs a, int nblk, int ld_lse) {
+__device__ __forceinline__ void f32_row(float4 (&x)[F32Layout<D>::C4], const float* X, int r, int n, int s) {
+  const float4* row = reinterpret_cast<const float4*>(X + size_t(r) * D);
+#pragma unroll
+  for (int m = 0; m < F32Layout<D>::C4; ++m) x[m] = r < n ? row[4 * m + s] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Streamed rows [r0, r0 + kF32Tile) of a [n][D] matrix into registers, zeros past n.
+template <int D>
+__device__ __forceinline__ void f32_fetch(float4 (&buf)[F32Layout<D>::LOADS], const float* X, int r0, int n) {
+#pragma unroll
+  for (int l = 0; l < F32Layout<D>::LOADS; ++l) {
+    const int idx = threadIdx.x + l * kF32Threads, r = r0 + idx / (D / 4);
+    buf[l] = r < n ? reinterpret_cast<const float4*>(X + size_t(r) * D)[idx % (D / 4)]
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void f32_store(float4* tile, const float4 (&buf)[F32Layout<D>::LOADS]) {
+#pragma unroll
+  for (int l = 0; l < F32Layout<D>::LOADS; ++l) tile[threadIdx.x + l * kF32Threads] = buf[l];
+}
+
+__device__ __forceinline__ float dot4(float4 x, float4 y, float acc) {
+  return fmaf(x.w, y.w, fmaf(x.z, y.z, fmaf(x.y, y.y, fmaf(x.x, y.x, acc))));
+}
+
+// Lane s of each quad: dot product of the quad's row with streamed row 4g + s.
+template <int D>
+__device__ __forceinline__ float quad_score(const float4 (&x)[F32Layout<D>::C4], const float4* tile, int g, int s) {
+  float u[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float4* row = tile + (4 * g + (r ^ s)) * (D / 4) + s;
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < F32Layout<D>::C4; ++m) acc = dot4(x[m], row[4 * m], acc);
+    u[r] = acc;
+  }
+  const float k0 = u[0] + dpp<kQuadSwap1>(u[1]);  // rows s and s ^ 2, two lanes each
+  const float k1 = u[2] + dpp<kQuadSwap1>(u[3]);
+  return k0 + dpp<kQuadSwap2>(k1);
+}
+
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, dpp<kQuadSwap1>(x));
+  return fmaxf(x, dpp<kQuadSwap2>(x));
+}
+
+// Value of lane R of the quad, in every lane of it.
+template <int R> __device__ __forceinline__ float quad_bcast(float x) { return dpp<R * 0x55>(x); }
+
+// Pass 1, fp32: per-row log2-sum-exp2 of the scaled causal scores.
+template <int D>
+__global__ __launch_bounds__(kF32Threads) void rowlse_f32(PrefillArgs a, int nblk, int ld_lse) {
+  using L = F32Layout<D>;
+  __shared__ float4 tile[L::TILE4];
   const int head = blockIdx.x / nblk;
-  const int i = (blockIdx.x % nblk) * 256 + threadIdx.x;
-  const int n = a.n;
-  if (i >= n) return;
+  const int qb = nblk - 1 - blockIdx.x % nblk;  // longest rows first
+  const int n = a.n, s = threadIdx.x & 3;
+  const int i = qb * kF32Rows + (threadIdx.x >> 2);
   const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
   const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
   const float c = a.c;
+  float4 q[L::C4];
+  f32_row<D>(q, Q, i, n, s);
+  const int ntiles = (min(n, (qb + 1) * kF32Rows) + kF32Tile - 1) / kF32Tile;
+  float4 buf[L::LOADS];
+  f32_fetch<D>(buf, K, 0, n);
   float m = kNegInf, l = 0.f;
-  for (int j = 0; j <= i; ++j) {
-    float s = 0.f;
-    for (int e = 0; e < D; ++e) s = fmaf(Q[size_t(i) * D + e], K[size_t(j) * D + e], s);
-    const float mn = fmaxf(m, s);
-    l = fmaf(l, fast_exp2((m - mn) * c), fast_exp2((s - mn) * c));
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    f32_store<D>(tile, buf);
+    __syncthreads();
+    if (t + 1 < ntiles) f32_fetch<D>(buf, K, (t + 1) * kF32Tile, n);
+    float sc[kF32Tile / 4];
+#pragma unroll
+    for (int g = 0; g < kF32Tile / 4; ++g) sc[g] = quad_score<D>(q, tile, g, s) * c;
+    if (t * kF32Tile + kF32Tile - 1 > qb * kF32Rows) {
+#pragma unroll
+      for (int g = 0; g < kF32Tile / 4; ++g)
+        if (t * kF32Tile + 4 * g + s > i) sc[g] = kNegInf;
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int g = 1; g < kF32Tile / 4; ++g) mt = fmaxf(mt, sc[g]);
+    const float mn = fmaxf(m, mt), ms = mn == kNegInf ? 0.f : mn;
+    float p = 0.f;
+#pragma unroll
+    for (int g = 0; g < kF32Tile / 4; ++g) p += fast_exp2(sc[g] - ms);
+    l = fmaf(l, fast_exp2(m - ms), p);
     m = mn;
   }
-  a.lse2[size_t(head) * ld_lse + i] = m * c + fast_log2(l);
+  const float M = quad_max(m);  // finite: key i lies in the row of lane i % 4
+  const float total = group_sum<4>(l * fast_exp2(m - M));
+  if (s == 0 && i < n) a.lse2[size_t(head) * ld_lse + i] = M + fast_log2(total);
 }
 
-// Pass 1 with output, fp32: one thread per query, its output row in registers.
+// Pass 1 with output, fp32: the quad keeps one running maximum so that its
+// four lanes can accumulate their columns of the output row together.
 template <int D>
-__global__ __launch_bounds__(256) void rowattn_valu(PrefillArgs a, int nblk, int ld_lse) {
+__global__ __launch_bounds__(kF32Threads) void rowattn_f32(PrefillArgs a, int nblk, int ld_lse) {
+  using L = F32Layout<D>;
+  __shared__ float4 ktile[L::TILE4];
+  __shared__ float4 vtile[L::TILE4];
   const int head = blockIdx.x / nblk;
-  const int i = (blockIdx.x % nblk) * 256 + threadIdx.x;
-  const int n = a.n;
-  if (i >= n) return;
+  const int qb = nblk - 1 - blockIdx.x % nblk;
+  const int n = a.n, s = threadIdx.x & 3;
+  const int i = qb * kF32Rows + (threadIdx.x >> 2);
   const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
   const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
   const float* V = static_cast<const float*>(a.V) + size_t(head) * n * D;
   const float c = a.c;
+  float4 q[L::C4], o[L::C4];
+  f32_row<D>(q, Q, i, n, s);
+#pragma unroll
+  for (int e = 0; e < L::C4; ++e) o[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int ntiles = (min(n, (qb + 1) * kF32Rows) + kF32Tile - 1) / kF32Tile;
+  float4 kbuf[L::LOADS], vbuf[L::LOADS];
+  f32_fetch<D>(kbuf, K, 0, n);
+  f32_fetch<D>(vbuf, V, 0, n);
   float m = kNegInf, l = 0.f;
-  float o[D];
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    f32_store<D>(ktile, kbuf);
+    f32_store<D>(vtile, vbuf);
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      f32_fetch<D>(kbuf, K, (t + 1) * kF32Tile, n);
+      f32_fetch<D>(vbuf, V, (t + 1) * kF32Tile, n);
+    }
+    float sc[kF32Tile / 4];
 #pragma unroll
-  for (int e = 0; e < D; ++e) o[e] = 0.f;
-  for (int j = 0; j <= i; ++j) {
-    float s = 0.f;
-    for (int e = 0; e < D; ++e) s = fmaf(Q[size_t(i) * D + e], K[size_t(j) * D + e], s);
-    const float mn = fmaxf(m, s);
-    const float alpha = fast_exp2((m - mn) * c), p = fast_exp2((s - mn) * c);
-    l = fmaf(l, alpha, p);
+    for (int g = 0; g < kF32Tile / 4; ++g) sc[g] = quad_score<D>(q, ktile, g, s) * c;
+    if (t * kF32Tile + kF32Tile - 1 > qb * kF32Rows) {
 #pragma unroll
-    for (int e = 0; e < D; ++e) o[e] = fmaf(o[e], alpha, p * V[size_t(j) * D + e]);
+      for (int g = 0; g < kF32Tile / 4; ++g)
+        if (t * kF32Tile + 4 * g + s > i) sc[g] = kNegInf;
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int g = 1; g < kF32Tile / 4; ++g) mt = fmaxf(mt, sc[g]);
+    const float mn = fmaxf(m, quad_max(mt)), ms = mn == kNegInf ? 0.f : mn;
+    const float alpha = fast_exp2(m - ms);
+    float psum = 0.f;
+#pragma unroll
+    for (int g = 0; g < kF32Tile / 4; ++g) {
+      sc[g] = fast_exp2(sc[g] - ms);
+      psum += sc[g];
+    }
+    l = fmaf(l, alpha, psum);
+#pragma unroll
+    for (int e = 0; e < L::C4; ++e) {
+      o[e].x *= alpha;
+      o[e].y *= alpha;
+      o[e].z *= alpha;
+      o[e].w *= alpha;
+    }
+#pragma unroll
+    for (int g = 0; g < kF32Tile / 4; ++g) {
+      const float p[4] = {quad_bcast<0>(sc[g]), quad_bcast<1>(sc[g]), quad_bcast<2>(sc[g]), quad_bcast<3>(sc[g])};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4* row = vtile + (4 * g + r) * (D / 4) + s;
+#pragma unroll
+        for (int e = 0; e < L::C4; ++e) {
+          const float4 y = row[4 * e];
+          o[e].x = fmaf(p[r], y.x, o[e].x);
+          o[e].y = fmaf(p[r], y.y, o[e].y);
+          o[e].z = fmaf(p[r], y.z, o[e].z);
+          o[e].w = fmaf(p[r], y.w, o[e].w);
+        }
+      }
+    }
     m = mn;
   }
-  const float lse2 = m * c + fast_log2(l);
-  a.lse2[size_t(head) * ld_lse + i] = lse2;
-  if (a.lse_out) a.lse_out[size_t(head) * n + i] = lse2 * 0.6931471805599453f;
-  const float inv = 1.0f / l;
-  float* orow = a.out + (size_t(head) * n + i) * D;
+  const float total = group_sum<4>(l);
+  if (i >= n) return;
+  const float lse2 = m + fast_log2(total);
+  if (s == 0) {
+    a.lse2[size_t(head) * ld_lse + i] = lse2;
+    if (a.lse_out) a.lse_out[size_t(head) * n + i] = lse2 * 0.6931471805599453f;
+  }
+  const float inv = 1.0f / total;
+  float4* orow = reinterpret_cast<float4*>(a.out + (size_t(head) * n + i) * D);
 #pragma unroll
-  for (int e = 0; e < D; ++e) orow[e] = o[e] * inv;
+  for (int e = 0; e < L::C4; ++e) orow[4 * e + s] = make_float4(o[e].x * inv, o[e].y * inv, o[e].z * inv, o[e].w * inv);
 }
 
 // Pass 1 replaced by the caller's natural-log normalisers: lse2 = lse * log2(e).
@@ -690,26 +845,55 @@ __global__ void lse_from_natural(PrefillArgs a, int G, int ld_lse) {
   }
 }
 
+// Pass 2, fp32: a workgroup owns 64 keys and streams the queries at and after
+// its first key, with their normalisers, through LDS.
 template <int D>
-__global__ __launch_bounds__(256) void colsum_valu(PrefillArgs a, int nblk, int ld_lse) {
+__global__ __launch_bounds__(kF32Threads) void colsum_f32(PrefillArgs a, int nblk, int ld_lse) {
+  using L = F32Layout<D>;
+  __shared__ float4 tile[L::TILE4];
+  __shared__ float ltile[kF32Tile];
   const int head = blockIdx.x / nblk;
-  const int j = (blockIdx.x % nblk) * 256 + threadIdx.x;
-  const int n = a.n;
-  if (j >= n) return;
+  const int kb = blockIdx.x % nblk;  // key block 0 streams the most queries
+  const int n = a.n, s = threadIdx.x & 3;
+  const int k0 = kb * kF32Rows, j = k0 + (threadIdx.x >> 2);
   const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
   const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
   const float* lse = a.lse2 + size_t(head) * ld_lse;
   const float c = a.c;
+  float4 kr[L::C4];
+  f32_row<D>(kr, K, j, n, s);
+  const int t0 = k0 / kF32Tile, ntiles = (n + kF32Tile - 1) / kF32Tile;
+  float4 buf[L::LOADS];
+  f32_fetch<D>(buf, Q, t0 * kF32Tile, n);
+  const int lr = threadIdx.x < kF32Tile ? t0 * kF32Tile + threadIdx.x : n;
+  float lbuf = lr < n ? lse[lr] : 0.f;
   float sum = 0.f, comp = 0.f;
-  for (int i = j; i < n; ++i) {
-    float s = 0.f;
-    for (int e = 0; e < D; ++e) s = fmaf(Q[size_t(i) * D + e], K[size_t(j) * D + e], s);
-    const float y = fast_exp2(fmaf(s, c, -lse[i])) - comp;
-    const float t = sum + y;
-    comp = (t - sum) - y;
-    sum = t;
+  for (int t = t0; t < ntiles; ++t) {
+    __syncthreads();
+    f32_store<D>(tile, buf);
+    if (threadIdx.x < kF32Tile) ltile[threadIdx.x] = lbuf;
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      f32_fetch<D>(buf, Q, (t + 1) * kF32Tile, n);
+      const int r = threadIdx.x < kF32Tile ? (t + 1) * kF32Tile + threadIdx.x : n;
+      lbuf = r < n ? lse[r] : 0.f;
+    }
+    const bool edge = t * kF32Tile < k0 + kF32Rows || (t + 1) * kF32Tile > n;
+#pragma unroll
+    for (int g = 0; g < kF32Tile / 4; ++g) {
+      float p = fast_exp2(fmaf(quad_score<D>(kr, tile, g, s), c, -ltile[4 * g + s]));
+      if (edge) {
+        const int qi = t * kF32Tile + 4 * g + s;
+        if (qi < j || qi >= n) p = 0.f;
+      }
+      const float y = p - comp;
+      const float u = sum + y;
+      comp = (u - sum) - y;
+      sum = u;
+    }
   }
-  a.colsum[size_t(head) * n + j] = sum - comp;
+  const float total = group_sum<4>(sum - comp);
+  if (s == 0 && j < n) a.colsum[size_t(head) * n + j] = total;
 }
 
 // ---------------------------------------------------------------- select + gather
@@ -962,19 +1146,20 @@ int pad8(int x) { return (x + 7) & ~7; }
 template <int DT, int D>
 hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
   const int ld_lse = (a.n + 63) & ~63;
-  const int nblk = (a.n + 255) / 256;
   if (a.pass1 == PASS1_GIVEN) {
     int64_t blocks = (int64_t(G) * a.n + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(lse_from_natural, dim3(unsigned(blocks)), dim3(256), 0, s, a, G, ld_lse);
   }
   if constexpr (DT == DT_F32) {
+    const int nblk = (a.n + kF32Rows - 1) / kF32Rows;
     if (a.pass1 == PASS1_LSE)
-      hipLaunchKernelGGL((rowlse_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
+      hipLaunchKernelGGL((rowlse_f32<D>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
     else if (a.pass1 == PASS1_ATTENTION)
-      hipLaunchKernelGGL((rowattn_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
-    hipLaunchKernelGGL((colsum_valu<D>), dim3(G * nblk), dim3(256), 0, s, a, nblk, ld_lse);
+      hipLaunchKernelGGL((rowattn_f32<D>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
+    hipLaunchKernelGGL((colsum_f32<D>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
   } else {
+    const int nblk = (a.n + 255) / 256;
     if (a.pass1 == PASS1_ATTENTION)
       hipLaunchKernelGGL((rowattn8_lds<DT, D>), dim3(pad8(G * nblk)), dim3(512), 0, s, a, nblk, G, ld_lse);
     // Prompts up to 2048 tokens: 2-wave workgroups (128 queries or keys), so

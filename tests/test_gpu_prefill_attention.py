@@ -6,7 +6,8 @@ The prompt's attention output is compared element by element (max-abs 2e-2
 for 16-bit inputs, 1e-4 for fp32) and its log normalisers to 1e-4 relative;
 the column sums, the selection and the decode steps that follow must meet the
 same bar as after h2o_prefill_select. Prompts span several 64-key tiles and
-256-query blocks with ragged tails, a single token, exactly one tile, both
+256-query blocks with ragged tails (fp32: several 64-row workgroups and
+32-row streamed tiles), a single token, exactly one tile, both
 head sizes and every input dtype; the named workloads run at full size with
 sampled heads.
 """
@@ -25,6 +26,8 @@ CASES = [
     ("ragged_f16_d64", 1, 5, 64, "f16", 517, 33, 34, 20),
     ("f32_d128", 1, 2, 128, "f32", 129, 16, 33, 10),
     ("f32_d64", 2, 1, 64, "f32", 70, 8, 8, 10),
+    ("f32_ragged_d128", 1, 3, 128, "f32", 461, 30, 30, 8),
+    ("f32_long_d64", 2, 2, 64, "f32", 1000, 50, 50, 8),
     ("one_token_bf16", 2, 1, 128, "bf16", 1, 1, 1, 10),
     ("one_tile_f16", 1, 2, 128, "f16", 64, 12, 12, 10),
     ("two_blocks_bf16_d64", 1, 2, 64, "bf16", 600, 40, 40, 10),
