@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA peak, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak, TFLOP/s (fp32 prompts run on the VALU)
 METRIC = "H2O decode head-steps/sec + achieved HBM GB/s (% of MI355X peak)"
 DECODE_SOURCES = {"fused": ["decode.hip", "h2o_device.h", "launch.h"],
                   "split": ["decode_split.hip", "h2o_device.h", "launch.h"],
@@ -472,7 +473,11 @@ def main():
                      "copy_note": "plain 1 GiB device-to-device copy (read + write bytes), 5 timed"},
         "decode_head_steps_per_s": head_steps / (median(decode_ms) / 1e3),
         "prefill": {"ms_per_layer": pf_s * 1e3, "algorithmic_TFLOPs": prefill_flops / pf_s / 1e12,
-                    "mfma_frac": prefill_flops / pf_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                    "mfma_frac": (prefill_flops / pf_s / 1e12 / MFMA_BF16_PEAK_TFLOPS) if wl.dtype != "f32" else None,
+                    "bound": "mfma" if wl.dtype != "f32" else "valu",
+                    "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS if wl.dtype != "f32" else FP32_VECTOR_PEAK_TFLOPS,
+                    "frac": prefill_flops / pf_s / 1e12 /
+                            (MFMA_BF16_PEAK_TFLOPS if wl.dtype != "f32" else FP32_VECTOR_PEAK_TFLOPS),
                     # one causal QK^T pass is the least any exact column sum needs
                     "one_pass_TFLOPs": 1.0 * n * (n + 1) * d * G / pf_s / 1e12,
                     # exp2 per score in each pass: n(n+1)/2 per head and pass
