@@ -637,6 +637,9 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
 constexpr int kF32Threads = 256;
 constexpr int kF32Rows = kF32Threads / 4;  // rows owned by a workgroup
 constexpr int kF32Tile = 32;               // streamed rows per LDS tile
+// Heads x prompt rows from which the column pass and the row pass without
+// output give each quad two rows (1024 two-row workgroups fill the chip).
+constexpr int64_t kF32TwoRowsMin = int64_t(1024) * 2 * kF32Rows;
 
 template <int D> struct F32Layout {
   static constexpr int C4 = D / 16;                   // float4 columns per lane
@@ -699,50 +702,111 @@ __device__ __forceinline__ float quad_max(float x) {
 // Value of lane R of the quad, in every lane of it.
 template <int R> __device__ __forceinline__ float quad_bcast(float x) { return dpp<R * 0x55>(x); }
 
+// R query rows per quad (rows r, r + 64, ...): each streamed float4 read from
+// LDS then feeds 4R FMAs, for prompts long enough to keep the chip busy with
+// 64R-row workgroups. All scores of a tile in one pass: lane s gets, for each
+// of its R rows, the score against streamed row 4g + s in out[h][g]. The
+// next streamed row's reads are issued ahead of the current row's FMAs in
+// program order (two register buffers); pinning that order with a scheduling
+// barrier raised the register count to two waves per SIMD and was 8% slower.
+template <int D, int R>
+__device__ __forceinline__ void tile_scores(const float4 (&x)[R][F32Layout<D>::C4], const float4* tile, int s,
+                                            float (&out)[R][kF32Tile / 4]) {
+  constexpr int C4 = F32Layout<D>::C4;
+  constexpr int NR = kF32Tile;  // (group, r) pairs per tile
+  float4 y[2][C4];
+  auto load = [&](float4 (&dst)[C4], int gr) {
+    const float4* row = tile + (4 * (gr >> 2) + ((gr & 3) ^ s)) * (D / 4) + s;
+#pragma unroll
+    for (int m = 0; m < C4; ++m) dst[m] = row[4 * m];
+  };
+  load(y[0], 0);
+  float u[R][4];
+#pragma unroll
+  for (int gr = 0; gr < NR; ++gr) {
+    if (gr + 1 < NR) load(y[(gr + 1) & 1], gr + 1);
+    const int r = gr & 3;
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < C4; ++m) acc = dot4(x[h][m], y[gr & 1][m], acc);
+      u[h][r] = acc;
+    }
+    if (r == 3) {
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        const float k0 = u[h][0] + dpp<kQuadSwap1>(u[h][1]);  // rows s and s ^ 2, two lanes each
+        const float k1 = u[h][2] + dpp<kQuadSwap1>(u[h][3]);
+        out[h][gr >> 2] = k0 + dpp<kQuadSwap2>(k1);
+      }
+    }
+  }
+}
+
 // Pass 1, fp32: per-row log2-sum-exp2 of the scaled causal scores.
-template <int D>
+template <int D, int R>
 __global__ __launch_bounds__(kF32Threads) void rowlse_f32(PrefillArgs a, int nblk, int ld_lse) {
   using L = F32Layout<D>;
+  constexpr int ROWS = R * kF32Rows;  // query rows per workgroup
   __shared__ float4 tile[L::TILE4];
   const int head = blockIdx.x / nblk;
   const int qb = nblk - 1 - blockIdx.x % nblk;  // longest rows first
   const int n = a.n, s = threadIdx.x & 3;
-  const int i = qb * kF32Rows + (threadIdx.x >> 2);
+  const int i0 = qb * ROWS + (threadIdx.x >> 2);  // rows i0 + h * kF32Rows
   const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
   const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
   const float c = a.c;
-  float4 q[L::C4];
-  f32_row<D>(q, Q, i, n, s);
-  const int ntiles = (min(n, (qb + 1) * kF32Rows) + kF32Tile - 1) / kF32Tile;
+  float4 q[R][L::C4];
+#pragma unroll
+  for (int h = 0; h < R; ++h) f32_row<D>(q[h], Q, i0 + h * kF32Rows, n, s);
+  const int ntiles = (min(n, (qb + 1) * ROWS) + kF32Tile - 1) / kF32Tile;
   float4 buf[L::LOADS];
   f32_fetch<D>(buf, K, 0, n);
-  float m = kNegInf, l = 0.f;
+  float m[R], l[R];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    m[h] = kNegInf;
+    l[h] = 0.f;
+  }
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();
     f32_store<D>(tile, buf);
     __syncthreads();
     if (t + 1 < ntiles) f32_fetch<D>(buf, K, (t + 1) * kF32Tile, n);
-    float sc[kF32Tile / 4];
+    float sc[R][kF32Tile / 4];
+    tile_scores<D, R>(q, tile, s, sc);
 #pragma unroll
-    for (int g = 0; g < kF32Tile / 4; ++g) sc[g] = quad_score<D>(q, tile, g, s) * c;
-    if (t * kF32Tile + kF32Tile - 1 > qb * kF32Rows) {
+    for (int h = 0; h < R; ++h)
 #pragma unroll
-      for (int g = 0; g < kF32Tile / 4; ++g)
-        if (t * kF32Tile + 4 * g + s > i) sc[g] = kNegInf;
+      for (int g = 0; g < kF32Tile / 4; ++g) sc[h][g] *= c;
+    if (t * kF32Tile + kF32Tile - 1 > qb * ROWS) {
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+#pragma unroll
+        for (int g = 0; g < kF32Tile / 4; ++g)
+          if (t * kF32Tile + 4 * g + s > i0 + h * kF32Rows) sc[h][g] = kNegInf;
     }
-    float mt = sc[0];
 #pragma unroll
-    for (int g = 1; g < kF32Tile / 4; ++g) mt = fmaxf(mt, sc[g]);
-    const float mn = fmaxf(m, mt), ms = mn == kNegInf ? 0.f : mn;
-    float p = 0.f;
+    for (int h = 0; h < R; ++h) {
+      float mt = sc[h][0];
 #pragma unroll
-    for (int g = 0; g < kF32Tile / 4; ++g) p += fast_exp2(sc[g] - ms);
-    l = fmaf(l, fast_exp2(m - ms), p);
-    m = mn;
+      for (int g = 1; g < kF32Tile / 4; ++g) mt = fmaxf(mt, sc[h][g]);
+      const float mn = fmaxf(m[h], mt), ms = mn == kNegInf ? 0.f : mn;
+      float p = 0.f;
+#pragma unroll
+      for (int g = 0; g < kF32Tile / 4; ++g) p += fast_exp2(sc[h][g] - ms);
+      l[h] = fmaf(l[h], fast_exp2(m[h] - ms), p);
+      m[h] = mn;
+    }
   }
-  const float M = quad_max(m);  // finite: key i lies in the row of lane i % 4
-  const float total = group_sum<4>(l * fast_exp2(m - M));
-  if (s == 0 && i < n) a.lse2[size_t(head) * ld_lse + i] = M + fast_log2(total);
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    const int i = i0 + h * kF32Rows;
+    const float M = quad_max(m[h]);  // finite: key i lies in the row of lane i % 4
+    const float total = group_sum<4>(l[h] * fast_exp2(m[h] - M));
+    if (s == 0 && i < n) a.lse2[size_t(head) * ld_lse + i] = M + fast_log2(total);
+  }
 }
 
 // Pass 1 with output, fp32: the quad keeps one running maximum so that its
@@ -845,29 +909,37 @@ __global__ void lse_from_natural(PrefillArgs a, int G, int ld_lse) {
   }
 }
 
-// Pass 2, fp32: a workgroup owns 64 keys and streams the queries at and after
-// its first key, with their normalisers, through LDS.
-template <int D>
+// Pass 2, fp32: a workgroup owns 64R keys (R per quad: keys j, j + 64, ...)
+// and streams the queries at and after its first key, with their
+// normalisers, through LDS.
+template <int D, int R>
 __global__ __launch_bounds__(kF32Threads) void colsum_f32(PrefillArgs a, int nblk, int ld_lse) {
   using L = F32Layout<D>;
+  constexpr int ROWS = R * kF32Rows;  // keys per workgroup
   __shared__ float4 tile[L::TILE4];
   __shared__ float ltile[kF32Tile];
   const int head = blockIdx.x / nblk;
   const int kb = blockIdx.x % nblk;  // key block 0 streams the most queries
   const int n = a.n, s = threadIdx.x & 3;
-  const int k0 = kb * kF32Rows, j = k0 + (threadIdx.x >> 2);
+  const int k0 = kb * ROWS, j0 = k0 + (threadIdx.x >> 2);  // keys j0 + h * kF32Rows
   const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
   const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
   const float* lse = a.lse2 + size_t(head) * ld_lse;
   const float c = a.c;
-  float4 kr[L::C4];
-  f32_row<D>(kr, K, j, n, s);
+  float4 kr[R][L::C4];
+#pragma unroll
+  for (int h = 0; h < R; ++h) f32_row<D>(kr[h], K, j0 + h * kF32Rows, n, s);
   const int t0 = k0 / kF32Tile, ntiles = (n + kF32Tile - 1) / kF32Tile;
   float4 buf[L::LOADS];
   f32_fetch<D>(buf, Q, t0 * kF32Tile, n);
   const int lr = threadIdx.x < kF32Tile ? t0 * kF32Tile + threadIdx.x : n;
   float lbuf = lr < n ? lse[lr] : 0.f;
-  float sum = 0.f, comp = 0.f;
+  float sum[R], comp[R];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    sum[h] = 0.f;
+    comp[h] = 0.f;
+  }
   for (int t = t0; t < ntiles; ++t) {
     __syncthreads();
     f32_store<D>(tile, buf);
@@ -878,22 +950,33 @@ __global__ __launch_bounds__(kF32Threads) void colsum_f32(PrefillArgs a, int nbl
       const int r = threadIdx.x < kF32Tile ? (t + 1) * kF32Tile + threadIdx.x : n;
       lbuf = r < n ? lse[r] : 0.f;
     }
-    const bool edge = t * kF32Tile < k0 + kF32Rows || (t + 1) * kF32Tile > n;
+    const bool edge = t * kF32Tile < k0 + ROWS || (t + 1) * kF32Tile > n;
+    float sc[R][kF32Tile / 4];
+    tile_scores<D, R>(kr, tile, s, sc);
 #pragma unroll
     for (int g = 0; g < kF32Tile / 4; ++g) {
-      float p = fast_exp2(fmaf(quad_score<D>(kr, tile, g, s), c, -ltile[4 * g + s]));
-      if (edge) {
-        const int qi = t * kF32Tile + 4 * g + s;
-        if (qi < j || qi >= n) p = 0.f;
+      float v[R];
+#pragma unroll
+      for (int h = 0; h < R; ++h) v[h] = sc[h][g];
+      const float lq = ltile[4 * g + s];
+      const int qi = t * kF32Tile + 4 * g + s;
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        float p = fast_exp2(fmaf(v[h], c, -lq));
+        if (edge && (qi < j0 + h * kF32Rows || qi >= n)) p = 0.f;
+        const float y = p - comp[h];
+        const float u = sum[h] + y;
+        comp[h] = (u - sum[h]) - y;
+        sum[h] = u;
       }
-      const float y = p - comp;
-      const float u = sum + y;
-      comp = (u - sum) - y;
-      sum = u;
     }
   }
-  const float total = group_sum<4>(sum - comp);
-  if (s == 0 && j < n) a.colsum[size_t(head) * n + j] = total;
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    const int j = j0 + h * kF32Rows;
+    const float total = group_sum<4>(sum[h] - comp[h]);
+    if (s == 0 && j < n) a.colsum[size_t(head) * n + j] = total;
+  }
 }
 
 // ---------------------------------------------------------------- select + gather
@@ -1153,11 +1236,22 @@ hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
   }
   if constexpr (DT == DT_F32) {
     const int nblk = (a.n + kF32Rows - 1) / kF32Rows;
-    if (a.pass1 == PASS1_LSE)
-      hipLaunchKernelGGL((rowlse_f32<D>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
-    else if (a.pass1 == PASS1_ATTENTION)
+    // Two rows per quad once the prompt gives every CU several 128-row
+    // workgroups; below that, one row keeps the workgroup count up.
+    const bool two = int64_t(G) * a.n >= kF32TwoRowsMin;
+    const int nblk2 = (a.n + 2 * kF32Rows - 1) / (2 * kF32Rows);
+    if (a.pass1 == PASS1_LSE) {
+      if (two)
+        hipLaunchKernelGGL((rowlse_f32<D, 2>), dim3(G * nblk2), dim3(kF32Threads), 0, s, a, nblk2, ld_lse);
+      else
+        hipLaunchKernelGGL((rowlse_f32<D, 1>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
+    } else if (a.pass1 == PASS1_ATTENTION) {
       hipLaunchKernelGGL((rowattn_f32<D>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
-    hipLaunchKernelGGL((colsum_f32<D>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
+    }
+    if (two)
+      hipLaunchKernelGGL((colsum_f32<D, 2>), dim3(G * nblk2), dim3(kF32Threads), 0, s, a, nblk2, ld_lse);
+    else
+      hipLaunchKernelGGL((colsum_f32<D, 1>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
   } else {
     const int nblk = (a.n + 255) / 256;
     if (a.pass1 == PASS1_ATTENTION)

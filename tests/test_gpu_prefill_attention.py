@@ -99,3 +99,21 @@ def test_prefill_attention_zero_queries_closed_form(gpu, dtype, n, batch):
         np.testing.assert_allclose(glse[j], np.log(rows), rtol=1e-5, atol=1e-5)
         np.testing.assert_allclose(gcol[j], Hn[n] - Hn[:n], rtol=1e-4)
     log(f"[attention] zero queries, {dtype} n={n}: closed form holds on {sample.size} heads")
+
+
+# fp32 prompts with at least 1024 x 128 head rows take the two-rows-per-quad
+# kernels (both head sizes); the GPU runs every head, the oracle checks a sample.
+@pytest.mark.parametrize("case", [("f32_two_rows_d128", 4, 32, 128, 1030, "select"),
+                                  ("f32_two_rows_d64", 8, 32, 64, 517, "select"),
+                                  ("f32_two_rows_attention", 4, 32, 128, 1030, "attention")],
+                         ids=lambda c: c[0])
+def test_prefill_f32_two_rows(gpu, case):
+    name, B, H, d, n, mode = case
+    assert B * H * n >= 1024 * 128
+    wl = Workload(name, B, H, d, "f32", n, 48, 48, 6, 1.5, 0.0, seed=zlib.crc32(name.encode()) % 10000)
+    run = ParityRun(wl, wl.steps, sample=sample_heads(wl, 6), label=f"{name} 6 heads")
+    run.prefill(mode=mode)
+    rep = run.decode()
+    log(f"[prefill {mode}] {name}: {rep}")
+    assert rep.steps == wl.steps
+
