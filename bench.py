@@ -55,6 +55,7 @@ def parse_args():
                    help="decode steps per bench step (default: the workload's own count; for profiling runs)")
     p.add_argument("--batch", type=int, default=None, help="override the workload's batch")
     p.add_argument("--heads", type=int, default=None, help="override the workload's heads")
+    p.add_argument("--prompt-len", type=int, default=None, help="override the workload's prompt length")
     p.add_argument("--decode", choices=("fused", "split"), default="fused",
                    help="decode entry point: h2o_decode_step (fused) or h2o_decode_step_split")
     p.add_argument("--chunk-rows", type=int, default=0, help="split decode chunk length (0 = library's choice)")
@@ -201,11 +202,13 @@ def main():
         wl = wl.with_(steps=max(1, min(args.decode_steps, wl.steps)))
     if args.batch is not None or args.heads is not None:
         wl = wl.with_(batch=args.batch or wl.batch, heads=args.heads or wl.heads)
+    if args.prompt_len is not None:
+        wl = wl.with_(prompt_len=args.prompt_len)
     if args.k_heavy is not None or args.k_recent is not None:
         wl = wl.with_(k_heavy=wl.k_heavy if args.k_heavy is None else args.k_heavy,
                       k_recent=wl.k_recent if args.k_recent is None else args.k_recent)
     policy = {"accumulated": 0, "averaged": 1, "position": 2}[args.policy]
-    default_shape = (args.batch is None and args.heads is None and args.k_heavy is None
+    default_shape = (args.batch is None and args.heads is None and args.prompt_len is None and args.k_heavy is None
                      and args.k_recent is None and args.policy == "accumulated")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
