@@ -520,7 +520,12 @@ hipError_t launch_typed(int G, const DecodeArgs& a, hipStream_t s) {
     // 256 slots; larger caches take 8, so that the epilogue loads nothing
     // from HBM up to 512 slots (OPT-30B shape, 410 slots: 62.0 -> 61.4 us).
     constexpr int UB = 4;
-    const int grid = G < resident ? G : resident;
+    // With more heads than two waves per SIMD, the grid fills a third: the
+    // scored kernel's 140-157 registers leave room for it, and one wave's
+    // epilogue then overlaps the others' streams (large-batch layer, 8192
+    // heads: 187.5 -> 185.5 us; a grid balanced to exactly three heads per
+    // wave measured 188.6 us).
+    const int grid = G < resident ? G : (SCORED ? (G < resident * 3 / 2 ? G : resident * 3 / 2) : resident);
     if (a.k > 256)
       hipLaunchKernelGGL((decode_wave_kernel<DT, D, UB, 8, WMINW, SCORED>), dim3(grid), dim3(64), shmem, s, a, G);
     else
