@@ -190,7 +190,7 @@ h2o_status split_step(h2o_cache* cache, const void* q, const void* k_new, const 
   const int Lmax = int(split_cmax(k)) * kSplitRows;
   if (L > Lmax) L = Lmax;
   const int chunks = nu > 0 ? (nu + L - 1) / L : 1;
-  if (chunks > split_cmax(k)) return fail(H2O_EINVAL, "chunk_rows %d too small for k = %d", L, k);
+  if (size_t(chunks) > split_cmax(k)) return fail(H2O_EINVAL, "chunk_rows %d too small for k = %d", L, k);
 
   h2o::DecodeArgs a{};
   a.K = cache->K;
