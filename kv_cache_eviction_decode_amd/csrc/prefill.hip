@@ -980,7 +980,11 @@ __global__ __launch_bounds__(kF32Threads) void colsum_f32(PrefillArgs a, int nbl
 }
 
 // ---------------------------------------------------------------- select + gather
-constexpr int kSelThreads = 1024;
+// 512 threads, the slot list sized to k in dynamic LDS (1 KiB at k = 256):
+// several heads' workgroups share a CU. Against 1024 threads and a list sized
+// for the largest cache: prompt 1024 prefill 1.04 -> 1.01 ms, 1920 2.38 ->
+// 2.35 ms, 16384 unchanged (256 threads: 1% slower there).
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 
 __device__ int block_exclusive_scan(int v, int* sm_wave, int& total) {
@@ -1023,7 +1027,7 @@ template <int N, int BITS> __device__ __forceinline__ void store_codes(uint8_t* 
 template <int DT, int D, int BITS>
 __global__ __launch_bounds__(kSelThreads) void select_gather(PrefillArgs a) {
   constexpr int E = Elem<DT>::bytes, ROW = D * E, LPR = ROW / 16;
-  __shared__ int slot_pos[8192];
+  extern __shared__ int slot_pos[];  // [k]
   __shared__ int hist[256];
   __shared__ int sm_wave[kSelWaves];
   __shared__ int sm_digit, sm_above, sm_P;
@@ -1274,19 +1278,19 @@ hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
   }
   switch (a.quant) {
     case H2O_QUANT_NONE:
-      hipLaunchKernelGGL((select_gather<DT, D, 0>), dim3(G), dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((select_gather<DT, D, 0>), dim3(G), dim3(kSelThreads), size_t(a.k_heavy + a.k_recent) * sizeof(int), s, a);
       break;
     case H2O_QUANT_U8:
       hipLaunchKernelGGL((key_grid<DT, D, 8>), dim3(G), dim3(256), 0, s, a);
-      hipLaunchKernelGGL((select_gather<DT, D, 8>), dim3(G), dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((select_gather<DT, D, 8>), dim3(G), dim3(kSelThreads), size_t(a.k_heavy + a.k_recent) * sizeof(int), s, a);
       break;
     case H2O_QUANT_U4:
       hipLaunchKernelGGL((key_grid<DT, D, 4>), dim3(G), dim3(256), 0, s, a);
-      hipLaunchKernelGGL((select_gather<DT, D, 4>), dim3(G), dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((select_gather<DT, D, 4>), dim3(G), dim3(kSelThreads), size_t(a.k_heavy + a.k_recent) * sizeof(int), s, a);
       break;
     case H2O_QUANT_U2:
       hipLaunchKernelGGL((key_grid<DT, D, 2>), dim3(G), dim3(256), 0, s, a);
-      hipLaunchKernelGGL((select_gather<DT, D, 2>), dim3(G), dim3(kSelThreads), 0, s, a);
+      hipLaunchKernelGGL((select_gather<DT, D, 2>), dim3(G), dim3(kSelThreads), size_t(a.k_heavy + a.k_recent) * sizeof(int), s, a);
       break;
     default:
       return hipErrorInvalidValue;
