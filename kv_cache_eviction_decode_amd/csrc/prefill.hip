@@ -145,126 +145,136 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // queries and run without the causal mask; only the last NW tiles (the
 // diagonal) test positions.
 template <int DT, int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
+__global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk, int G, int ld_lse, int paired) {
   using T = Tile64<DT, D, NW>;
   constexpr int QBLK = 64 * NW;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) char lds[2][T::BYTES];
+  const int per_head = paired ? (nblk + 1) / 2 : nblk;
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
-  if (L >= G * nblk) return;  // uniform over the workgroup
-  const int head = L / nblk;
-  const int qb = nblk - 1 - L % nblk;  // longest causal extent first
+  if (L >= G * per_head) return;  // uniform over the workgroup
+  const int head = L / per_head;
+  const int pr = L % per_head;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lh = lane >> 5;
   const int n = a.n;
-  const int wg_q0 = qb * QBLK;
-  const int q0 = wg_q0 + wave * 64;
   const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
   const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
   const auto Kr = T::rows(Kh, n);
   const float c = a.c;
 
-  // The first key tile is fetched together with the query fragments, so the
-  // prologue waits for one memory latency, not two.
-  uint4 nx[T::CPT];
-  T::fetch(nx, Kr, 0);
-  uint4 qf[2][T::KS];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int r = min(q0 + cb * 32 + (lane & 31), n - 1);
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
-  }
-  wait_vmem_all();
-  float ref[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
-  const int ntiles = min(wg_q0 + QBLK - 1, n - 1) / 64 + 1;
-  const int nfull = min(wg_q0 / 64, ntiles);  // tiles with every key <= the workgroup's first query
-  T::store(lds[0], nx);
-  __syncthreads();
+  // Paired: query blocks nblk - 1 - pr and pr, one after the other, whose
+  // causal extents add up to nblk + 1 blocks whatever pr is, so every
+  // workgroup carries the same work (an odd middle block runs alone).
+  // Otherwise block nblk - 1 - pr alone (longest causal extent first).
+  for (int seg = 0; seg < 2; ++seg) {
+    const int qb = seg == 0 ? nblk - 1 - pr : pr;
+    if (seg == 1 && (!paired || qb == nblk - 1 - pr)) break;
+    const int wg_q0 = qb * QBLK;
+    const int q0 = wg_q0 + wave * 64;
 
-  auto accumulate = [&](const f32x16 (&acc)[2][2], int cb) {
-    const float nr = -ref[cb];
-    float t0 = 0.f, t1 = 0.f;
+    // The first key tile is fetched together with the query fragments, so the
+    // prologue waits for one memory latency, not two.
+    uint4 nx[T::CPT];
+    T::fetch(nx, Kr, 0);
+    uint4 qf[2][T::KS];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      t0 += fast_exp2(fmaf(acc[0][cb][j], c, nr));
-      t1 += fast_exp2(fmaf(acc[1][cb][j], c, nr));
+    for (int cb = 0; cb < 2; ++cb) {
+      const int r = min(q0 + cb * 32 + (lane & 31), n - 1);
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
     }
-    const float t = t0 + t1;
-    if (t <= 0x1p64f) {
-      l[cb] += t;
-    } else {  // first tile (reference -inf), or a score far above the reference; also NaN
-      float tm = kNegInf;
+    wait_vmem_all();
+    float ref[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+    const int ntiles = min(wg_q0 + QBLK - 1, n - 1) / 64 + 1;
+    const int nfull = min(wg_q0 / 64, ntiles);  // tiles with every key <= the workgroup's first query
+    T::store(lds[0], nx);
+    __syncthreads();
+
+    auto accumulate = [&](const f32x16 (&acc)[2][2], int cb) {
+      const float nr = -ref[cb];
+      float t0 = 0.f, t1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][cb][j], acc[0][cb][j + 1]);
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
-      const float rn = fmaxf(ref[cb], tm * c);
-      if (rn != kNegInf) {
-        float u0 = 0.f, u1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          u0 += fast_exp2(fmaf(acc[0][cb][j], c, -rn));
-          u1 += fast_exp2(fmaf(acc[1][cb][j], c, -rn));
-        }
-        l[cb] = fmaf(l[cb], fast_exp2(ref[cb] - rn), u0 + u1);
-        ref[cb] = rn;
+      for (int j = 0; j < 16; ++j) {
+        t0 += fast_exp2(fmaf(acc[0][cb][j], c, nr));
+        t1 += fast_exp2(fmaf(acc[1][cb][j], c, nr));
       }
-    }
-  };
-
-  auto step = [&](int kt, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    if (kt + 1 < ntiles) T::fetch(nx, Kr, (kt + 1) * 64);
-    const char* buf = lds[kt & 1];
-    const int key0 = kt * 64;
-    if (!MASKED || key0 <= min(q0 + 63, n - 1)) {  // some key of the tile is visible to this wave
-      // The MFMA chain issues at raised priority, so that while this wave
-      // feeds the matrix unit the other wave of the SIMD fills the gaps with
-      // its exp/sum work instead of delaying the chain (long prompts: 5%).
-      __builtin_amdgcn_s_setprio(1);
-      f32x16 acc[2][2];
+      const float t = t0 + t1;
+      if (t <= 0x1p64f) {
+        l[cb] += t;
+      } else {  // first tile (reference -inf), or a score far above the reference; also NaN
+        float tm = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        uint4 af[T::KS];
+        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][cb][j], acc[0][cb][j + 1]);
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, kb, ks, lane);
+        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
+        const float rn = fmaxf(ref[cb], tm * c);
+        if (rn != kNegInf) {
+          float u0 = 0.f, u1 = 0.f;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          acc[kb][cb] = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < T::KS; ++ks) acc[kb][cb] = MfmaOp<DT>::run(af[ks], qf[cb][ks], acc[kb][cb]);
+          for (int j = 0; j < 16; ++j) {
+            u0 += fast_exp2(fmaf(acc[0][cb][j], c, -rn));
+            u1 += fast_exp2(fmaf(acc[1][cb][j], c, -rn));
+          }
+          l[cb] = fmaf(l[cb], fast_exp2(ref[cb] - rn), u0 + u1);
+          ref[cb] = rn;
         }
       }
-      __builtin_amdgcn_s_setprio(0);
-      // acc[kb][cb][j] = s(query q0 + 32cb + lane%32, key key0 + 32kb + mfma_row(j))
+    };
+
+    auto step = [&](int kt, auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+      if (kt + 1 < ntiles) T::fetch(nx, Kr, (kt + 1) * 64);
+      const char* buf = lds[kt & 1];
+      const int key0 = kt * 64;
+      if (!MASKED || key0 <= min(q0 + 63, n - 1)) {  // some key of the tile is visible to this wave
+        // The MFMA chain issues at raised priority, so that while this wave
+        // feeds the matrix unit the other wave of the SIMD fills the gaps with
+        // its exp/sum work instead of delaying the chain (long prompts: 5%).
+        __builtin_amdgcn_s_setprio(1);
+        f32x16 acc[2][2];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        if constexpr (MASKED) {
-          const int qi = q0 + cb * 32 + (lane & 31);
-          if (key0 + 63 > q0 + cb * 32) {  // tile reaches past some query of this block
+        for (int kb = 0; kb < 2; ++kb) {
+          uint4 af[T::KS];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+          for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, kb, ks, lane);
 #pragma unroll
-              for (int j = 0; j < 16; ++j)
-                if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][cb][j] = kNegInf;
+          for (int cb = 0; cb < 2; ++cb) {
+            acc[kb][cb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks) acc[kb][cb] = MfmaOp<DT>::run(af[ks], qf[cb][ks], acc[kb][cb]);
           }
         }
-        accumulate(acc, cb);
-      }
-    }
-    if (kt + 1 < ntiles) T::store(lds[(kt + 1) & 1], nx);
-    __syncthreads();
-  };
-  for (int kt = 0; kt < nfull; ++kt) step(kt, std::false_type{});
-  for (int kt = nfull; kt < ntiles; ++kt) step(kt, std::true_type{});
+        __builtin_amdgcn_s_setprio(0);
+        // acc[kb][cb][j] = s(query q0 + 32cb + lane%32, key key0 + 32kb + mfma_row(j))
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const float ro = __shfl_xor(ref[cb], 32);
-    const float lo = __shfl_xor(l[cb], 32);
-    const float M = fmaxf(ref[cb], ro);
-    const float Lsum = l[cb] * fast_exp2(ref[cb] - M) + lo * fast_exp2(ro - M);
-    const int qi = q0 + cb * 32 + (lane & 31);
-    if (lh == 0 && qi < n) a.lse2[size_t(head) * ld_lse + qi] = M + fast_log2(Lsum);
+        for (int cb = 0; cb < 2; ++cb) {
+          if constexpr (MASKED) {
+            const int qi = q0 + cb * 32 + (lane & 31);
+            if (key0 + 63 > q0 + cb * 32) {  // tile reaches past some query of this block
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                  if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][cb][j] = kNegInf;
+            }
+          }
+          accumulate(acc, cb);
+        }
+      }
+      if (kt + 1 < ntiles) T::store(lds[(kt + 1) & 1], nx);
+      __syncthreads();
+    };
+    for (int kt = 0; kt < nfull; ++kt) step(kt, std::false_type{});
+    for (int kt = nfull; kt < ntiles; ++kt) step(kt, std::true_type{});
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float ro = __shfl_xor(ref[cb], 32);
+      const float lo = __shfl_xor(l[cb], 32);
+      const float M = fmaxf(ref[cb], ro);
+      const float Lsum = l[cb] * fast_exp2(ref[cb] - M) + lo * fast_exp2(ro - M);
+      const int qi = q0 + cb * 32 + (lane & 31);
+      if (lh == 0 && qi < n) a.lse2[size_t(head) * ld_lse + qi] = M + fast_log2(Lsum);
+    }
   }
 }
 
@@ -497,130 +507,139 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
 // tiles together with their lse2. Each lane owns one key column; the tile
 // partial of 32 values is added with compensation.
 template <int DT, int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
+__global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk, int G, int ld_lse, int paired) {
   using T = Tile64<DT, D, NW>;
   constexpr int KBLK = 64 * NW;  // keys per workgroup
   __shared__ __attribute__((aligned(16))) char lds[2][T::BYTES];
   __shared__ __attribute__((aligned(16))) float lds_lse[2][64];
+  const int per_head = paired ? (nblk + 1) / 2 : nblk;
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
-  if (L >= G * nblk) return;
-  const int head = L / nblk;
-  const int kblk = L % nblk;  // smallest key block = most query tiles, first
+  if (L >= G * per_head) return;
+  const int head = L / per_head;
+  const int pr = L % per_head;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lh = lane >> 5;
   const int n = a.n;
-  const int wg_k0 = kblk * KBLK;
-  const int k0 = wg_k0 + wave * 64;
   const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
   const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
   const auto Qr = T::rows(Qh, n);
   const float* lse = a.lse2 + size_t(head) * ld_lse;
   const float c = a.c;
 
-  const int t0 = wg_k0 / 64;
-  const int ntiles = (n + 63) / 64;
-  uint4 nx[T::CPT];
-  float nl = 0.f;
-  // Rows past the prompt get lse = +inf, so their terms are exp2(-inf) = 0
-  // without a per-element test.
-  auto fetch = [&](int qt) {
-    T::fetch(nx, Qr, qt * 64);
-    if (threadIdx.x < 64) {
-      const int q = qt * 64 + threadIdx.x;
-      nl = q < n ? lse[q] : __builtin_huge_valf();
-    }
-  };
-  auto store = [&](int buf) {
-    T::store(lds[buf], nx);
-    if (threadIdx.x < 64) lds_lse[buf][threadIdx.x] = nl;
-  };
-  // The first query tile is fetched together with the key fragments, so the
-  // prologue waits for one memory latency, not two.
-  fetch(t0);
-  uint4 kf[2][T::KS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int r = min(k0 + kb * 32 + (lane & 31), n - 1);
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) kf[kb][ks] = ld16(Kh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
-  }
-  wait_vmem_all();
-  float sum[2] = {0.f, 0.f}, comp[2] = {0.f, 0.f};
-  store(0);
-  __syncthreads();
-  auto step = [&](int qt, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    const int cur = (qt - t0) & 1;
-    if (qt + 1 < ntiles) fetch(qt + 1);
-    const int qrow0 = qt * 64;
-    if (!MASKED || (qrow0 + 63 >= k0 && k0 < n)) {  // some query of the tile sees a key of this wave
-      const char* buf = lds[cur];
-      __builtin_amdgcn_s_setprio(1);  // as in rowlse_lds (neutral here, kept for symmetry)
-      f32x16 acc[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        uint4 af[T::KS];
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, qb, ks, lane);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          acc[qb][kb] = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < T::KS; ++ks) acc[qb][kb] = MfmaOp<DT>::run(af[ks], kf[kb][ks], acc[qb][kb]);
-        }
+  // Paired: key blocks pr and nblk - 1 - pr, one after the other (the same
+  // total number of query tiles for every workgroup; an odd middle block
+  // alone). Otherwise block pr alone (most query tiles first).
+  for (int seg = 0; seg < 2; ++seg) {
+    const int kblk = seg == 0 ? pr : nblk - 1 - pr;
+    if (seg == 1 && (!paired || kblk == pr)) break;
+    const int wg_k0 = kblk * KBLK;
+    const int k0 = wg_k0 + wave * 64;
+
+    const int t0 = wg_k0 / 64;
+    const int ntiles = (n + 63) / 64;
+    uint4 nx[T::CPT];
+    float nl = 0.f;
+    // Rows past the prompt get lse = +inf, so their terms are exp2(-inf) = 0
+    // without a per-element test.
+    auto fetch = [&](int qt) {
+      T::fetch(nx, Qr, qt * 64);
+      if (threadIdx.x < 64) {
+        const int q = qt * 64 + threadIdx.x;
+        nl = q < n ? lse[q] : __builtin_huge_valf();
       }
-      __builtin_amdgcn_s_setprio(0);
-      // acc[qb][kb][j] = s(query qrow0 + 32qb + mfma_row(j), key k0 + 32kb + lane%32)
-      float lq[2][16];
+    };
+    auto store = [&](int buf) {
+      T::store(lds[buf], nx);
+      if (threadIdx.x < 64) lds_lse[buf][threadIdx.x] = nl;
+    };
+    // The first query tile is fetched together with the key fragments, so the
+    // prologue waits for one memory latency, not two.
+    fetch(t0);
+    uint4 kf[2][T::KS];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = min(k0 + kb * 32 + (lane & 31), n - 1);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float4 v = *reinterpret_cast<const float4*>(&lds_lse[cur][qb * 32 + 8 * jj + 4 * lh]);
-          lq[qb][4 * jj] = v.x;
-          lq[qb][4 * jj + 1] = v.y;
-          lq[qb][4 * jj + 2] = v.z;
-          lq[qb][4 * jj + 3] = v.w;
-        }
+      for (int ks = 0; ks < T::KS; ++ks) kf[kb][ks] = ld16(Kh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
+    }
+    wait_vmem_all();
+    float sum[2] = {0.f, 0.f}, comp[2] = {0.f, 0.f};
+    store(0);
+    __syncthreads();
+    auto step = [&](int qt, auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+      const int cur = (qt - t0) & 1;
+      if (qt + 1 < ntiles) fetch(qt + 1);
+      const int qrow0 = qt * 64;
+      if (!MASKED || (qrow0 + 63 >= k0 && k0 < n)) {  // some query of the tile sees a key of this wave
+        const char* buf = lds[cur];
+        __builtin_amdgcn_s_setprio(1);  // as in rowlse_lds (neutral here, kept for symmetry)
+        f32x16 acc[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if constexpr (MASKED) {
-          const int kj = k0 + kb * 32 + (lane & 31);
-          if (qrow0 < k0 + kb * 32 + 31) {  // diagonal tile: queries before the key see nothing
+        for (int qb = 0; qb < 2; ++qb) {
+          uint4 af[T::KS];
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+          for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, qb, ks, lane);
 #pragma unroll
-              for (int j = 0; j < 16; ++j)
-                acc[qb][kb][j] = qrow0 + qb * 32 + mfma_row(j, lane) < kj ? kNegInf : acc[qb][kb][j];
+          for (int kb = 0; kb < 2; ++kb) {
+            acc[qb][kb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks) acc[qb][kb] = MfmaOp<DT>::run(af[ks], kf[kb][ks], acc[qb][kb]);
           }
         }
-        float t = 0.f, t2 = 0.f;
+        __builtin_amdgcn_s_setprio(0);
+        // acc[qb][kb][j] = s(query qrow0 + 32qb + mfma_row(j), key k0 + 32kb + lane%32)
+        float lq[2][16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          t += fast_exp2(fmaf(acc[0][kb][j], c, -lq[0][j]));
-          t2 += fast_exp2(fmaf(acc[1][kb][j], c, -lq[1][j]));
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float4 v = *reinterpret_cast<const float4*>(&lds_lse[cur][qb * 32 + 8 * jj + 4 * lh]);
+            lq[qb][4 * jj] = v.x;
+            lq[qb][4 * jj + 1] = v.y;
+            lq[qb][4 * jj + 2] = v.z;
+            lq[qb][4 * jj + 3] = v.w;
+          }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if constexpr (MASKED) {
+            const int kj = k0 + kb * 32 + (lane & 31);
+            if (qrow0 < k0 + kb * 32 + 31) {  // diagonal tile: queries before the key see nothing
+#pragma unroll
+              for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                  acc[qb][kb][j] = qrow0 + qb * 32 + mfma_row(j, lane) < kj ? kNegInf : acc[qb][kb][j];
+            }
+          }
+          float t = 0.f, t2 = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            t += fast_exp2(fmaf(acc[0][kb][j], c, -lq[0][j]));
+            t2 += fast_exp2(fmaf(acc[1][kb][j], c, -lq[1][j]));
+          }
+          t += t2;
+          const float y = t - comp[kb];
+          const float s2 = sum[kb] + y;
+          comp[kb] = (s2 - sum[kb]) - y;
+          sum[kb] = s2;
         }
-        t += t2;
-        const float y = t - comp[kb];
-        const float s2 = sum[kb] + y;
-        comp[kb] = (s2 - sum[kb]) - y;
-        sum[kb] = s2;
       }
-    }
-    if (qt + 1 < ntiles) store(cur ^ 1);
-    __syncthreads();
-  };
-  // Query tiles [t0, t0 + NW) hold the diagonal of some wave of the
-  // workgroup; every later tile is visible to all of its keys.
-  const int tdiag = min(t0 + NW, ntiles);
-  for (int qt = t0; qt < tdiag; ++qt) step(qt, std::true_type{});
-  for (int qt = tdiag; qt < ntiles; ++qt) step(qt, std::false_type{});
+      if (qt + 1 < ntiles) store(cur ^ 1);
+      __syncthreads();
+    };
+    // Query tiles [t0, t0 + NW) hold the diagonal of some wave of the
+    // workgroup; every later tile is visible to all of its keys.
+    const int tdiag = min(t0 + NW, ntiles);
+    for (int qt = t0; qt < tdiag; ++qt) step(qt, std::true_type{});
+    for (int qt = tdiag; qt < ntiles; ++qt) step(qt, std::false_type{});
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const float mine = sum[kb] - comp[kb];
-    const float other = __shfl_xor(mine, 32);
-    const int kj = k0 + kb * 32 + (lane & 31);
-    if (lh == 0 && kj < n) a.colsum[size_t(head) * n + kj] = mine + other;
+    for (int kb = 0; kb < 2; ++kb) {
+      const float mine = sum[kb] - comp[kb];
+      const float other = __shfl_xor(mine, 32);
+      const int kj = k0 + kb * 32 + (lane & 31);
+      if (lh == 0 && kj < n) a.colsum[size_t(head) * n + kj] = mine + other;
+    }
   }
 }
 
@@ -1230,6 +1249,14 @@ __global__ void cache_clear(float* score, int32_t* pos, int64_t count) {
 
 int pad8(int x) { return (x + 7) & ~7; }
 
+// Whether the scoring passes pair a head's blocks i and nblk - 1 - i in one
+// workgroup: for an even block count every workgroup then carries the same
+// work (prompt 1024: 1.00-1.04 -> 0.93-0.95 ms; 1536: -7%; 2048: -4%; 4096:
+// -5%). An odd count leaves the middle block alone, and there pairing
+// measured the same or up to 3% slower (1152, 1920, 3840), so it is kept
+// for even counts only.
+int pair_blocks(int nblk) { return nblk >= 2 && nblk % 2 == 0 ? 1 : 0; }
+
 template <int DT, int D>
 hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
   const int ld_lse = (a.n + 63) & ~63;
@@ -1267,13 +1294,17 @@ hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
     // 8192: 5%).
     if (a.n <= 2048) {
       const int nb = (a.n + 127) / 128;
+      const int paired = pair_blocks(nb);
+      const int per_head = paired ? (nb + 1) / 2 : nb;
       if (a.pass1 == PASS1_LSE)
-        hipLaunchKernelGGL((rowlse_lds<DT, D, 2>), dim3(pad8(G * nb)), dim3(128), 0, s, a, nb, G, ld_lse);
-      hipLaunchKernelGGL((colsum_lds<DT, D, 2>), dim3(pad8(G * nb)), dim3(128), 0, s, a, nb, G, ld_lse);
+        hipLaunchKernelGGL((rowlse_lds<DT, D, 2>), dim3(pad8(G * per_head)), dim3(128), 0, s, a, nb, G, ld_lse, paired);
+      hipLaunchKernelGGL((colsum_lds<DT, D, 2>), dim3(pad8(G * per_head)), dim3(128), 0, s, a, nb, G, ld_lse, paired);
     } else {
+      const int paired = pair_blocks(nblk);
+      const int per_head = paired ? (nblk + 1) / 2 : nblk;
       if (a.pass1 == PASS1_LSE)
-        hipLaunchKernelGGL((rowlse_lds<DT, D, 4>), dim3(pad8(G * nblk)), dim3(256), 0, s, a, nblk, G, ld_lse);
-      hipLaunchKernelGGL((colsum_lds<DT, D, 4>), dim3(pad8(G * nblk)), dim3(256), 0, s, a, nblk, G, ld_lse);
+        hipLaunchKernelGGL((rowlse_lds<DT, D, 4>), dim3(pad8(G * per_head)), dim3(256), 0, s, a, nblk, G, ld_lse, paired);
+      hipLaunchKernelGGL((colsum_lds<DT, D, 4>), dim3(pad8(G * per_head)), dim3(256), 0, s, a, nblk, G, ld_lse, paired);
     }
   }
   switch (a.quant) {

@@ -31,6 +31,7 @@ CASES = [
     ("one_token_bf16", 2, 1, 128, "bf16", 1, 1, 1, 10),
     ("one_tile_f16", 1, 2, 128, "f16", 64, 12, 12, 10),
     ("two_blocks_bf16_d64", 1, 2, 64, "bf16", 600, 40, 40, 10),
+    ("paired_blocks_bf16", 2, 3, 128, "bf16", 200, 20, 20, 10),  # blocks 0 and 1 in one workgroup
 ]
 
 

@@ -44,6 +44,8 @@ CASES = [
     ("f16_2wave_d64", "f16", 64, 600, [(130, 4.0), (400, 16.0), (599, 32.0)]),
     ("bf16_4wave", "bf16", 128, 2300, [(700, 2.0), (1500, 8.0), (2100, 16.0)]),
     ("f16_4wave", "f16", 128, 2300, [(700, 2.0), (1500, 8.0), (2100, 16.0)]),
+    # 10 blocks of 256: paired blocks (i, 9 - i) with a ragged last block
+    ("bf16_4wave_paired", "bf16", 128, 2500, [(700, 2.0), (1500, 8.0), (2400, 16.0)]),
 ]
 
 
