@@ -143,7 +143,8 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 //
 // Key tiles below the workgroup's first query are visible to all of its
 // queries and run without the causal mask; only the last NW tiles (the
-// diagonal) test positions.
+// diagonal) test positions, and there a wave skips the MFMAs and the exp
+// work of every 32x32 quarter that lies wholly above the diagonal.
 template <int DT, int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk, int G, int ld_lse, int paired) {
   using T = Tile64<DT, D, NW>;
@@ -170,7 +171,11 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
     const int qb = seg == 0 ? nblk - 1 - pr : pr;
     if (seg == 1 && (!paired || qb == nblk - 1 - pr)) break;
     const int wg_q0 = qb * QBLK;
-    const int q0 = wg_q0 + wave * 64;
+    // The wave's 64 queries are two 32-row halves of the block, w and
+    // 2NW - 1 - w: on the causal diagonal every wave then sees the same
+    // number of keys, so no wave waits at the tile barrier while another
+    // finishes a longer diagonal.
+    const int qh[2] = {wg_q0 + 32 * wave, wg_q0 + 32 * (2 * NW - 1 - wave)};
 
     // The first key tile is fetched together with the query fragments, so the
     // prologue waits for one memory latency, not two.
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
     uint4 qf[2][T::KS];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const int r = min(q0 + cb * 32 + (lane & 31), n - 1);
+      const int r = min(qh[cb] + (lane & 31), n - 1);
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) qf[cb][ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
     }
@@ -190,13 +195,16 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
     T::store(lds[0], nx);
     __syncthreads();
 
-    auto accumulate = [&](const f32x16 (&acc)[2][2], int cb) {
+    // Adds half cb's scores of the tile (both 32-key halves, or the first
+    // only when the second lies wholly past the queries).
+    auto accumulate = [&](const f32x16 (&acc)[2][2], int cb, auto both_halves) {
+      constexpr bool BOTH = decltype(both_halves)::value;
       const float nr = -ref[cb];
       float t0 = 0.f, t1 = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         t0 += fast_exp2(fmaf(acc[0][cb][j], c, nr));
-        t1 += fast_exp2(fmaf(acc[1][cb][j], c, nr));
+        if constexpr (BOTH) t1 += fast_exp2(fmaf(acc[1][cb][j], c, nr));
       }
       const float t = t0 + t1;
       if (t <= 0x1p64f) {
@@ -205,15 +213,17 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
         float tm = kNegInf;
 #pragma unroll
         for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][cb][j], acc[0][cb][j + 1]);
+        if constexpr (BOTH) {
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
+          for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][cb][j], acc[1][cb][j + 1]);
+        }
         const float rn = fmaxf(ref[cb], tm * c);
         if (rn != kNegInf) {
           float u0 = 0.f, u1 = 0.f;
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             u0 += fast_exp2(fmaf(acc[0][cb][j], c, -rn));
-            u1 += fast_exp2(fmaf(acc[1][cb][j], c, -rn));
+            if constexpr (BOTH) u1 += fast_exp2(fmaf(acc[1][cb][j], c, -rn));
           }
           l[cb] = fmaf(l[cb], fast_exp2(ref[cb] - rn), u0 + u1);
           ref[cb] = rn;
@@ -226,40 +236,54 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
       if (kt + 1 < ntiles) T::fetch(nx, Kr, (kt + 1) * 64);
       const char* buf = lds[kt & 1];
       const int key0 = kt * 64;
-      if (!MASKED || key0 <= min(q0 + 63, n - 1)) {  // some key of the tile is visible to this wave
-        // The MFMA chain issues at raised priority, so that while this wave
-        // feeds the matrix unit the other wave of the SIMD fills the gaps with
-        // its exp/sum work instead of delaying the chain (long prompts: 5%).
-        __builtin_amdgcn_s_setprio(1);
-        f32x16 acc[2][2];
+      // vis[kb][cb]: the 32 keys key0 + 32kb.. reach some query of half cb
+      // (past the prompt's end a half has no queries). The second query half
+      // lies after the first, so vis[kb][0] implies vis[kb][1], and the
+      // second key half lies after the first, so vis[1][cb] implies vis[0][cb].
+      bool vis[2][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          uint4 af[T::KS];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, kb, ks, lane);
+        for (int cb = 0; cb < 2; ++cb) vis[kb][cb] = !MASKED || key0 + 32 * kb <= min(qh[cb] + 31, n - 1);
+      // The MFMA chain issues at raised priority, so that while this wave
+      // feeds the matrix unit the other wave of the SIMD fills the gaps with
+      // its exp/sum work instead of delaying the chain (long prompts: 5%).
+      __builtin_amdgcn_s_setprio(1);
+      f32x16 acc[2][2];
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            acc[kb][cb] = f32x16{};
+      for (int kb = 0; kb < 2; ++kb) {
+        if (!vis[kb][0] && !vis[kb][1]) continue;
+        uint4 af[T::KS];
 #pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks) acc[kb][cb] = MfmaOp<DT>::run(af[ks], qf[cb][ks], acc[kb][cb]);
-          }
-        }
-        __builtin_amdgcn_s_setprio(0);
-        // acc[kb][cb][j] = s(query q0 + 32cb + lane%32, key key0 + 32kb + mfma_row(j))
+        for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, kb, ks, lane);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
-          if constexpr (MASKED) {
-            const int qi = q0 + cb * 32 + (lane & 31);
-            if (key0 + 63 > q0 + cb * 32) {  // tile reaches past some query of this block
+          if (!vis[kb][cb]) continue;
+          acc[kb][cb] = f32x16{};
 #pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                  if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][cb][j] = kNegInf;
-            }
-          }
-          accumulate(acc, cb);
+          for (int ks = 0; ks < T::KS; ++ks) acc[kb][cb] = MfmaOp<DT>::run(af[ks], qf[cb][ks], acc[kb][cb]);
         }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // acc[kb][cb][j] = s(query qh[cb] + lane%32, key key0 + 32kb + mfma_row(j))
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        if (!vis[0][cb]) continue;
+        if constexpr (MASKED) {
+          // Keys and query halves are 32-aligned, so a quarter is cut by the
+          // diagonal only when it starts at the half's first query.
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (vis[kb][cb] && key0 + 32 * kb == qh[cb]) {
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                if (mfma_row(j, lane) > (lane & 31)) acc[kb][cb][j] = kNegInf;
+            }
+        }
+        if (vis[1][cb])
+          accumulate(acc, cb, std::true_type{});
+        else
+          accumulate(acc, cb, std::false_type{});
       }
       if (kt + 1 < ntiles) T::store(lds[(kt + 1) & 1], nx);
       __syncthreads();
@@ -272,7 +296,7 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
       const float lo = __shfl_xor(l[cb], 32);
       const float M = fmaxf(ref[cb], ro);
       const float Lsum = l[cb] * fast_exp2(ref[cb] - M) + lo * fast_exp2(ro - M);
-      const int qi = q0 + cb * 32 + (lane & 31);
+      const int qi = qh[cb] + (lane & 31);
       if (lh == 0 && qi < n) a.lse2[size_t(head) * ld_lse + qi] = M + fast_log2(Lsum);
     }
   }
@@ -505,7 +529,9 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
 // Pass 2: c_j = sum_{i>=j} 2^(c*s_ij - lse2_i). Workgroup = 64 * NW keys (64
 // per wave, held in registers as MFMA B operands); queries streamed in 64-row LDS
 // tiles together with their lse2. Each lane owns one key column; the tile
-// partial of 32 values is added with compensation.
+// partial of 32 values is added with compensation. On the first NW query
+// tiles (the diagonal) a wave skips every 32x32 quarter whose queries all
+// precede its keys.
 template <int DT, int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk, int G, int ld_lse, int paired) {
   using T = Tile64<DT, D, NW>;
@@ -533,7 +559,10 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
     const int kblk = seg == 0 ? pr : nblk - 1 - pr;
     if (seg == 1 && (!paired || kblk == pr)) break;
     const int wg_k0 = kblk * KBLK;
-    const int k0 = wg_k0 + wave * 64;
+    // The wave's 64 keys are two 32-row halves of the block, w and
+    // 2NW - 1 - w, so that on the causal diagonal every wave sees the same
+    // number of queries (as the query halves of rowlse_lds).
+    const int kh[2] = {wg_k0 + 32 * wave, wg_k0 + 32 * (2 * NW - 1 - wave)};
 
     const int t0 = wg_k0 / 64;
     const int ntiles = (n + 63) / 64;
@@ -558,7 +587,7 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
     uint4 kf[2][T::KS];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int r = min(k0 + kb * 32 + (lane & 31), n - 1);
+      const int r = min(kh[kb] + (lane & 31), n - 1);
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) kf[kb][ks] = ld16(Kh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
     }
@@ -571,59 +600,75 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
       const int cur = (qt - t0) & 1;
       if (qt + 1 < ntiles) fetch(qt + 1);
       const int qrow0 = qt * 64;
-      if (!MASKED || (qrow0 + 63 >= k0 && k0 < n)) {  // some query of the tile sees a key of this wave
-        const char* buf = lds[cur];
-        __builtin_amdgcn_s_setprio(1);  // as in rowlse_lds (neutral here, kept for symmetry)
-        f32x16 acc[2][2];
+      // vis[qb][kb]: some query of the 32 from qrow0 + 32qb sees a key of
+      // half kb (a half wholly past the prompt's end sees none). Later query
+      // halves see more, so vis[0][kb] implies vis[1][kb]; the second key
+      // half lies after the first, so vis[qb][1] implies vis[qb][0].
+      bool vis[2][2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          uint4 af[T::KS];
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, qb, ks, lane);
+        for (int kb = 0; kb < 2; ++kb) vis[qb][kb] = !MASKED || (kh[kb] < n && qrow0 + 32 * qb + 31 >= kh[kb]);
+      const char* buf = lds[cur];
+      __builtin_amdgcn_s_setprio(1);  // as in rowlse_lds (neutral here, kept for symmetry)
+      f32x16 acc[2][2];
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            acc[qb][kb] = f32x16{};
+      for (int qb = 0; qb < 2; ++qb) {
+        if (!vis[qb][0] && !vis[qb][1]) continue;
+        uint4 af[T::KS];
 #pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks) acc[qb][kb] = MfmaOp<DT>::run(af[ks], kf[kb][ks], acc[qb][kb]);
-          }
-        }
-        __builtin_amdgcn_s_setprio(0);
-        // acc[qb][kb][j] = s(query qrow0 + 32qb + mfma_row(j), key k0 + 32kb + lane%32)
-        float lq[2][16];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float4 v = *reinterpret_cast<const float4*>(&lds_lse[cur][qb * 32 + 8 * jj + 4 * lh]);
-            lq[qb][4 * jj] = v.x;
-            lq[qb][4 * jj + 1] = v.y;
-            lq[qb][4 * jj + 2] = v.z;
-            lq[qb][4 * jj + 3] = v.w;
-          }
+        for (int ks = 0; ks < T::KS; ++ks) af[ks] = T::frag(buf, qb, ks, lane);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if constexpr (MASKED) {
-            const int kj = k0 + kb * 32 + (lane & 31);
-            if (qrow0 < k0 + kb * 32 + 31) {  // diagonal tile: queries before the key see nothing
+          if (!vis[qb][kb]) continue;
+          acc[qb][kb] = f32x16{};
 #pragma unroll
-              for (int qb = 0; qb < 2; ++qb)
+          for (int ks = 0; ks < T::KS; ++ks) acc[qb][kb] = MfmaOp<DT>::run(af[ks], kf[kb][ks], acc[qb][kb]);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // acc[qb][kb][j] = s(query qrow0 + 32qb + mfma_row(j), key kh[kb] + lane%32)
+      float lq[2][16];
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                  acc[qb][kb][j] = qrow0 + qb * 32 + mfma_row(j, lane) < kj ? kNegInf : acc[qb][kb][j];
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float4 v = *reinterpret_cast<const float4*>(&lds_lse[cur][qb * 32 + 8 * jj + 4 * lh]);
+          lq[qb][4 * jj] = v.x;
+          lq[qb][4 * jj + 1] = v.y;
+          lq[qb][4 * jj + 2] = v.z;
+          lq[qb][4 * jj + 3] = v.w;
+        }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (!vis[1][kb]) continue;
+        if constexpr (MASKED) {
+          // 32-aligned halves: a quarter is cut by the diagonal only when
+          // its queries start at the key half's first key.
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            if (vis[qb][kb] && qrow0 + 32 * qb == kh[kb]) {
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                if (mfma_row(j, lane) < (lane & 31)) acc[qb][kb][j] = kNegInf;
             }
-          }
-          float t = 0.f, t2 = 0.f;
+        }
+        float t = 0.f, t2 = 0.f;
+        if (vis[0][kb]) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             t += fast_exp2(fmaf(acc[0][kb][j], c, -lq[0][j]));
             t2 += fast_exp2(fmaf(acc[1][kb][j], c, -lq[1][j]));
           }
-          t += t2;
-          const float y = t - comp[kb];
-          const float s2 = sum[kb] + y;
-          comp[kb] = (s2 - sum[kb]) - y;
-          sum[kb] = s2;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) t2 += fast_exp2(fmaf(acc[1][kb][j], c, -lq[1][j]));
         }
+        t += t2;
+        const float y = t - comp[kb];
+        const float s2 = sum[kb] + y;
+        comp[kb] = (s2 - sum[kb]) - y;
+        sum[kb] = s2;
       }
       if (qt + 1 < ntiles) store(cur ^ 1);
       __syncthreads();
@@ -637,7 +682,7 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
     for (int kb = 0; kb < 2; ++kb) {
       const float mine = sum[kb] - comp[kb];
       const float other = __shfl_xor(mine, 32);
-      const int kj = k0 + kb * 32 + (lane & 31);
+      const int kj = kh[kb] + (lane & 31);
       if (lh == 0 && kj < n) a.colsum[size_t(head) * n + kj] = mine + other;
     }
   }
