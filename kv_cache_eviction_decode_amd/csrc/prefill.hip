@@ -373,21 +373,20 @@ struct VTile8 {
 };
 
 template <int DT, int D>
-__global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, int G, int ld_lse) {
+__global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, int G, int ld_lse, int paired) {
   using T = Tile64<DT, D, 8>;
   using VT = VTile8<DT, D>;
   constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) char lds_k[2][T::BYTES];
   __shared__ __attribute__((aligned(16))) char lds_v[2][VT::BYTES];
+  const int per_head = paired ? (nblk + 1) / 2 : nblk;
   const int L = xcd_logical_block(blockIdx.x, gridDim.x);
-  if (L >= G * nblk) return;  // uniform over the workgroup
-  const int head = L / nblk;
-  const int qb = nblk - 1 - L % nblk;  // longest causal extent first
+  if (L >= G * per_head) return;  // uniform over the workgroup
+  const int head = L / per_head;
+  const int pr = L % per_head;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lh = lane >> 5;
   const int n = a.n;
-  const int wg_q0 = qb * 256;
-  const int q0 = wg_q0 + wave * 32;
   const char* Qh = static_cast<const char*>(a.Q) + size_t(head) * n * T::ROW;
   const char* Kh = static_cast<const char*>(a.K) + size_t(head) * n * T::ROW;
   const char* Vh = static_cast<const char*>(a.V) + size_t(head) * n * T::ROW;
@@ -395,134 +394,143 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
   const auto Vr = T::rows(Vh, n);
   const float c = a.c;
 
-  // The first key and value tiles are fetched together with the query
-  // fragments (one memory latency in the prologue, not two).
-  uint4 nk[T::CPT], nv[T::CPT];
-  T::fetch(nk, Kr, 0);
-  T::fetch(nv, Vr, 0);
-  uint4 qf[T::KS];
-  {
-    const int r = min(q0 + (lane & 31), n - 1);
+  // Blocks nblk - 1 - pr and pr in turn when paired (as in rowlse_lds),
+  // else block nblk - 1 - pr alone (longest causal extent first).
+  for (int seg = 0; seg < 2; ++seg) {
+    const int qb = seg == 0 ? nblk - 1 - pr : pr;
+    if (seg == 1 && (!paired || qb == nblk - 1 - pr)) break;
+    const int wg_q0 = qb * 256;
+    const int q0 = wg_q0 + wave * 32;
+
+    // The first key and value tiles are fetched together with the query
+    // fragments (one memory latency in the prologue, not two).
+    uint4 nk[T::CPT], nv[T::CPT];
+    T::fetch(nk, Kr, 0);
+    T::fetch(nv, Vr, 0);
+    uint4 qf[T::KS];
+    {
+      const int r = min(q0 + (lane & 31), n - 1);
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) qf[ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
-  }
-  wait_vmem_all();
-  f32x16 o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  float ref = kNegInf, l = 0.f;
-  const int ntiles = min(wg_q0 + 255, n - 1) / 64 + 1;
-  T::store(lds_k[0], nk);
-  VT::store(lds_v[0], nv);
-  __syncthreads();
-  const int qi = q0 + (lane & 31);
-  // Key tiles below the workgroup's first query need no causal mask.
-  const int nfull = min(wg_q0 / 64, ntiles);
-  auto step = [&](int kt, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    if (kt + 1 < ntiles) {
-      T::fetch(nk, Kr, (kt + 1) * 64);
-      T::fetch(nv, Vr, (kt + 1) * 64);
+      for (int ks = 0; ks < T::KS; ++ks) qf[ks] = ld16(Qh + size_t(r) * T::ROW + (ks * 16 + lh * 8) * T::E);
     }
-    const char* kbuf = lds_k[kt & 1];
-    const char* vbuf = lds_v[kt & 1];
-    const int key0 = kt * 64;
-    if (!MASKED || key0 <= min(q0 + 31, n - 1)) {  // every query of this wave sees key0
-      f32x16 acc[2];
+    wait_vmem_all();
+    f32x16 o[NDB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        acc[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) acc[kb] = MfmaOp<DT>::run(T::frag(kbuf, kb, ks, lane), qf[ks], acc[kb]);
-      }
-      // acc[kb][j] = s(query qi, key key0 + 32kb + mfma_row(j))
-      if constexpr (MASKED) {
-        if (key0 + 63 > q0) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][j] = kNegInf;
-        }
-      }
-      // Probabilities against the query's reference (base 2, shared by the
-      // two lane halves that hold the query's keys).
-      float p[2][16];
-      float t = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          p[kb][j] = fast_exp2(fmaf(acc[kb][j], c, -ref));
-          t += p[kb][j];
-        }
-      // P feeds the MFMA in the input type: fp16 must stay below its 65504
-      // limit, bf16 has fp32's range.
-      constexpr float kBound = DT == DT_F16 ? 0x1p15f : 0x1p64f;
-      const bool redo = !(t + __shfl_xor(t, 32) <= kBound);  // first tile, far above, or NaN
-      if (__ballot(redo)) {
-        float tm = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][j], acc[0][j + 1]);
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][j], acc[1][j + 1]);
-        const float tmax = fmaxf(tm, __shfl_xor(tm, 32)) * c;
-        float rn = redo ? fmaxf(ref, tmax) : ref;
-        if (rn == kNegInf) rn = 0.f;  // no visible key yet: nothing to scale
-        const float alpha = fast_exp2(ref - rn);  // 1 where the reference stays
-        if (redo) {
-          t = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              p[kb][j] = fast_exp2(fmaf(acc[kb][j], c, -rn));
-              t += p[kb][j];
-            }
-        }
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-        ref = rn;
-      }
-      l += t;
-      uint4 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        pb[kb][0] = pack8<DT>(p[kb]);
-        pb[kb][1] = pack8<DT>(p[kb] + 8);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            o[db] = MfmaOp<DT>::run(VT::frag(vbuf, db, kb * 2 + g, lane), pb[kb][g], o[db]);
-    }
-    if (kt + 1 < ntiles) {
-      T::store(lds_k[(kt + 1) & 1], nk);
-      VT::store(lds_v[(kt + 1) & 1], nv);
-    }
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    float ref = kNegInf, l = 0.f;
+    const int ntiles = min(wg_q0 + 255, n - 1) / 64 + 1;
+    T::store(lds_k[0], nk);
+    VT::store(lds_v[0], nv);
     __syncthreads();
-  };
-  for (int kt = 0; kt < nfull; ++kt) step(kt, std::false_type{});
-  for (int kt = nfull; kt < ntiles; ++kt) step(kt, std::true_type{});
-  const float lt = l + __shfl_xor(l, 32);  // both halves share the reference maximum
-  if (qi < n) {
-    const float lse2 = ref + fast_log2(lt);
-    if (lh == 0) {
-      a.lse2[size_t(head) * ld_lse + qi] = lse2;
-      if (a.lse_out) a.lse_out[size_t(head) * n + qi] = lse2 * 0.6931471805599453f;
+    const int qi = q0 + (lane & 31);
+    // Key tiles below the workgroup's first query need no causal mask.
+    const int nfull = min(wg_q0 / 64, ntiles);
+    auto step = [&](int kt, auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+      if (kt + 1 < ntiles) {
+        T::fetch(nk, Kr, (kt + 1) * 64);
+        T::fetch(nv, Vr, (kt + 1) * 64);
+      }
+      const char* kbuf = lds_k[kt & 1];
+      const char* vbuf = lds_v[kt & 1];
+      const int key0 = kt * 64;
+      if (!MASKED || key0 <= min(q0 + 31, n - 1)) {  // every query of this wave sees key0
+        f32x16 acc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          acc[kb] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < T::KS; ++ks) acc[kb] = MfmaOp<DT>::run(T::frag(kbuf, kb, ks, lane), qf[ks], acc[kb]);
+        }
+        // acc[kb][j] = s(query qi, key key0 + 32kb + mfma_row(j))
+        if constexpr (MASKED) {
+          if (key0 + 63 > q0) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int j = 0; j < 16; ++j)
+                if (key0 + kb * 32 + mfma_row(j, lane) > qi) acc[kb][j] = kNegInf;
+          }
+        }
+        // Probabilities against the query's reference (base 2, shared by the
+        // two lane halves that hold the query's keys).
+        float p[2][16];
+        float t = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            p[kb][j] = fast_exp2(fmaf(acc[kb][j], c, -ref));
+            t += p[kb][j];
+          }
+        // P feeds the MFMA in the input type: fp16 must stay below its 65504
+        // limit, bf16 has fp32's range.
+        constexpr float kBound = DT == DT_F16 ? 0x1p15f : 0x1p64f;
+        const bool redo = !(t + __shfl_xor(t, 32) <= kBound);  // first tile, far above, or NaN
+        if (__ballot(redo)) {
+          float tm = kNegInf;
+#pragma unroll
+          for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[0][j], acc[0][j + 1]);
+#pragma unroll
+          for (int j = 0; j < 16; j += 2) tm = max3f(tm, acc[1][j], acc[1][j + 1]);
+          const float tmax = fmaxf(tm, __shfl_xor(tm, 32)) * c;
+          float rn = redo ? fmaxf(ref, tmax) : ref;
+          if (rn == kNegInf) rn = 0.f;  // no visible key yet: nothing to scale
+          const float alpha = fast_exp2(ref - rn);  // 1 where the reference stays
+          if (redo) {
+            t = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int j = 0; j < 16; ++j) {
+                p[kb][j] = fast_exp2(fmaf(acc[kb][j], c, -rn));
+                t += p[kb][j];
+              }
+          }
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+          ref = rn;
+        }
+        l += t;
+        uint4 pb[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          pb[kb][0] = pack8<DT>(p[kb]);
+          pb[kb][1] = pack8<DT>(p[kb] + 8);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+              o[db] = MfmaOp<DT>::run(VT::frag(vbuf, db, kb * 2 + g, lane), pb[kb][g], o[db]);
+      }
+      if (kt + 1 < ntiles) {
+        T::store(lds_k[(kt + 1) & 1], nk);
+        VT::store(lds_v[(kt + 1) & 1], nv);
+      }
+      __syncthreads();
+    };
+    for (int kt = 0; kt < nfull; ++kt) step(kt, std::false_type{});
+    for (int kt = nfull; kt < ntiles; ++kt) step(kt, std::true_type{});
+    const float lt = l + __shfl_xor(l, 32);  // both halves share the reference maximum
+    if (qi < n) {
+      const float lse2 = ref + fast_log2(lt);
+      if (lh == 0) {
+        a.lse2[size_t(head) * ld_lse + qi] = lse2;
+        if (a.lse_out) a.lse_out[size_t(head) * n + qi] = lse2 * 0.6931471805599453f;
+      }
+      const float inv = 1.0f / lt;
+      float* orow = a.out + (size_t(head) * n + qi) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<float4*>(orow + db * 32 + 8 * jj + 4 * lh) =
+              make_float4(o[db][4 * jj] * inv, o[db][4 * jj + 1] * inv, o[db][4 * jj + 2] * inv, o[db][4 * jj + 3] * inv);
     }
-    const float inv = 1.0f / lt;
-    float* orow = a.out + (size_t(head) * n + qi) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *reinterpret_cast<float4*>(orow + db * 32 + 8 * jj + 4 * lh) =
-            make_float4(o[db][4 * jj] * inv, o[db][4 * jj + 1] * inv, o[db][4 * jj + 2] * inv, o[db][4 * jj + 3] * inv);
   }
 }
 
@@ -1294,12 +1302,13 @@ __global__ void cache_clear(float* score, int32_t* pos, int64_t count) {
 
 int pad8(int x) { return (x + 7) & ~7; }
 
-// Whether the scoring passes pair a head's blocks i and nblk - 1 - i in one
+// Whether the prefill passes pair a head's blocks i and nblk - 1 - i in one
 // workgroup: for an even block count every workgroup then carries the same
-// work (prompt 1024: 1.00-1.04 -> 0.93-0.95 ms; 1536: -7%; 2048: -4%; 4096:
-// -5%). An odd count leaves the middle block alone, and there pairing
-// measured the same or up to 3% slower (1152, 1920, 3840), so it is kept
-// for even counts only.
+// work (scoring, prompt 1024: 1.00-1.04 -> 0.93-0.95 ms; 1536: -7%; 2048:
+// -4%; 4096: -5%; with the prompt's attention output, 1024: -9%, 2048: -7%,
+// 4096: -4%). An odd count leaves the middle block alone, and there pairing
+// measured the same or up to 3% slower (1152, 1920, 3840 with 128- and
+// 256-row blocks), so it is kept for even counts only.
 int pair_blocks(int nblk) { return nblk >= 2 && nblk % 2 == 0 ? 1 : 0; }
 
 template <int DT, int D>
@@ -1330,8 +1339,11 @@ hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((colsum_f32<D, 1>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
   } else {
     const int nblk = (a.n + 255) / 256;
-    if (a.pass1 == PASS1_ATTENTION)
-      hipLaunchKernelGGL((rowattn8_lds<DT, D>), dim3(pad8(G * nblk)), dim3(512), 0, s, a, nblk, G, ld_lse);
+    if (a.pass1 == PASS1_ATTENTION) {
+      const int paired = pair_blocks(nblk);
+      hipLaunchKernelGGL((rowattn8_lds<DT, D>), dim3(pad8(G * (paired ? (nblk + 1) / 2 : nblk))), dim3(512), 0, s, a, nblk, G,
+                         ld_lse, paired);
+    }
     // Prompts up to 2048 tokens: 2-wave workgroups (128 queries or keys), so
     // that more, shorter workgroups overlap their prologues and fewer waves
     // idle on the causal diagonal (prompt 1024: 10% faster, 1920: 11%);
