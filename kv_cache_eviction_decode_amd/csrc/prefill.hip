@@ -127,6 +127,15 @@ __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf
 // for the next tile's prefetch inside the MFMA chain, exposing its latency.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Block pairing of the causal passes. Workgroup pr (0 <= pr < (nblk + 1) / 2)
+// takes the block with the (pr+1)-th longest causal extent, nblk - 1 - pr,
+// and then the block returned here (-1: none). Block b spans b + 1 block
+// lengths of keys. With an even count the partner of nblk - 1 - pr is pr,
+// and each workgroup spans nblk + 1; with an odd count the longest block
+// runs alone and the rest pair as (nblk - 1 - pr, pr - 1), each pair
+// spanning nblk, the longest block's extent.
+__device__ __forceinline__ int pair_partner(int nblk, int pr) { return (nblk & 1) ? pr - 1 : pr; }
+
 // Pass 1: lse2_i = log2 sum_{j<=i} 2^(c*s_ij). Workgroup = 64 * NW queries (64
 // per wave); keys streamed in 64-row LDS tiles. The transposed tile (keys x
 // queries) gives each lane one query column, so the row statistics are
@@ -163,13 +172,13 @@ __global__ __launch_bounds__(64 * NW, 2) void rowlse_lds(PrefillArgs a, int nblk
   const auto Kr = T::rows(Kh, n);
   const float c = a.c;
 
-  // Paired: query blocks nblk - 1 - pr and pr, one after the other, whose
-  // causal extents add up to nblk + 1 blocks whatever pr is, so every
-  // workgroup carries the same work (an odd middle block runs alone).
+  // Paired: query block nblk - 1 - pr, then block pair_partner(pr): the two
+  // causal extents add up to that of the longest block (odd count) or to
+  // one block more (even count), so every workgroup carries the same work.
   // Otherwise block nblk - 1 - pr alone (longest causal extent first).
   for (int seg = 0; seg < 2; ++seg) {
-    const int qb = seg == 0 ? nblk - 1 - pr : pr;
-    if (seg == 1 && (!paired || qb == nblk - 1 - pr)) break;
+    const int qb = seg == 0 ? nblk - 1 - pr : pair_partner(nblk, pr);
+    if (seg == 1 && (!paired || qb < 0)) break;
     const int wg_q0 = qb * QBLK;
     // The wave's 64 queries are two 32-row halves of the block, w and
     // 2NW - 1 - w: on the causal diagonal every wave then sees the same
@@ -394,11 +403,11 @@ __global__ __launch_bounds__(512, 1) void rowattn8_lds(PrefillArgs a, int nblk, 
   const auto Vr = T::rows(Vh, n);
   const float c = a.c;
 
-  // Blocks nblk - 1 - pr and pr in turn when paired (as in rowlse_lds),
-  // else block nblk - 1 - pr alone (longest causal extent first).
+  // Blocks nblk - 1 - pr and pair_partner(pr) in turn when paired (as in
+  // rowlse_lds), else block nblk - 1 - pr alone (longest causal extent first).
   for (int seg = 0; seg < 2; ++seg) {
-    const int qb = seg == 0 ? nblk - 1 - pr : pr;
-    if (seg == 1 && (!paired || qb == nblk - 1 - pr)) break;
+    const int qb = seg == 0 ? nblk - 1 - pr : pair_partner(nblk, pr);
+    if (seg == 1 && (!paired || qb < 0)) break;
     const int wg_q0 = qb * 256;
     const int q0 = wg_q0 + wave * 32;
 
@@ -560,12 +569,13 @@ __global__ __launch_bounds__(64 * NW, 2) void colsum_lds(PrefillArgs a, int nblk
   const float* lse = a.lse2 + size_t(head) * ld_lse;
   const float c = a.c;
 
-  // Paired: key blocks pr and nblk - 1 - pr, one after the other (the same
-  // total number of query tiles for every workgroup; an odd middle block
-  // alone). Otherwise block pr alone (most query tiles first).
+  // Paired: key block pr, then block nblk - 1 - pair_partner(pr) (the same
+  // total number of query tiles for every workgroup, as for the query blocks
+  // of rowlse_lds). Otherwise block pr alone (most query tiles first).
   for (int seg = 0; seg < 2; ++seg) {
-    const int kblk = seg == 0 ? pr : nblk - 1 - pr;
-    if (seg == 1 && (!paired || kblk == pr)) break;
+    const int partner = pair_partner(nblk, pr);
+    const int kblk = seg == 0 ? pr : nblk - 1 - partner;
+    if (seg == 1 && (!paired || partner < 0)) break;
     const int wg_k0 = kblk * KBLK;
     // The wave's 64 keys are two 32-row halves of the block, w and
     // 2NW - 1 - w, so that on the causal diagonal every wave sees the same
@@ -1302,14 +1312,11 @@ __global__ void cache_clear(float* score, int32_t* pos, int64_t count) {
 
 int pad8(int x) { return (x + 7) & ~7; }
 
-// Whether the prefill passes pair a head's blocks i and nblk - 1 - i in one
-// workgroup: for an even block count every workgroup then carries the same
-// work (scoring, prompt 1024: 1.00-1.04 -> 0.93-0.95 ms; 1536: -7%; 2048:
-// -4%; 4096: -5%; with the prompt's attention output, 1024: -9%, 2048: -7%,
-// 4096: -4%). An odd count leaves the middle block alone, and there pairing
-// measured the same or up to 3% slower (1152, 1920, 3840 with 128- and
-// 256-row blocks), so it is kept for even counts only.
-int pair_blocks(int nblk) { return nblk >= 2 && nblk % 2 == 0 ? 1 : 0; }
+// Whether the prefill passes pair a head's blocks in one workgroup (see
+// pair_partner): every workgroup then carries the same work (scoring, prompt
+// 1024: 1.00-1.04 -> 0.93-0.95 ms; 1536: -7%; 2048: -4%; 4096: -5%; with the
+// prompt's attention output, 1024: -9%, 2048: -7%, 4096: -4%).
+int pair_blocks(int nblk) { return nblk >= 2 ? 1 : 0; }
 
 template <int DT, int D>
 hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
