@@ -828,158 +828,171 @@ __device__ __forceinline__ void tile_scores(const float4 (&x)[R][F32Layout<D>::C
 
 // Pass 1, fp32: per-row log2-sum-exp2 of the scaled causal scores.
 template <int D, int R>
-__global__ __launch_bounds__(kF32Threads) void rowlse_f32(PrefillArgs a, int nblk, int ld_lse) {
+__global__ __launch_bounds__(kF32Threads) void rowlse_f32(PrefillArgs a, int nblk, int ld_lse, int paired) {
   using L = F32Layout<D>;
   constexpr int ROWS = R * kF32Rows;  // query rows per workgroup
   __shared__ float4 tile[L::TILE4];
-  const int head = blockIdx.x / nblk;
-  const int qb = nblk - 1 - blockIdx.x % nblk;  // longest rows first
+  const int per_head = paired ? (nblk + 1) / 2 : nblk;
+  const int head = blockIdx.x / per_head;
+  const int pr = blockIdx.x % per_head;
   const int n = a.n, s = threadIdx.x & 3;
-  const int i0 = qb * ROWS + (threadIdx.x >> 2);  // rows i0 + h * kF32Rows
   const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
   const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
   const float c = a.c;
-  float4 q[R][L::C4];
+  // Row blocks nblk - 1 - pr, then pair_partner(pr) when paired (as in
+  // rowlse_lds); unpaired, the longest rows first.
+  for (int seg = 0; seg < 2; ++seg) {
+    const int qb = seg == 0 ? nblk - 1 - pr : pair_partner(nblk, pr);
+    if (seg == 1 && (!paired || qb < 0)) break;
+    const int i0 = qb * ROWS + (threadIdx.x >> 2);  // rows i0 + h * kF32Rows
+    float4 q[R][L::C4];
 #pragma unroll
-  for (int h = 0; h < R; ++h) f32_row<D>(q[h], Q, i0 + h * kF32Rows, n, s);
-  const int ntiles = (min(n, (qb + 1) * ROWS) + kF32Tile - 1) / kF32Tile;
-  float4 buf[L::LOADS];
-  f32_fetch<D>(buf, K, 0, n);
-  float m[R], l[R];
+    for (int h = 0; h < R; ++h) f32_row<D>(q[h], Q, i0 + h * kF32Rows, n, s);
+    const int ntiles = (min(n, (qb + 1) * ROWS) + kF32Tile - 1) / kF32Tile;
+    float4 buf[L::LOADS];
+    f32_fetch<D>(buf, K, 0, n);
+    float m[R], l[R];
 #pragma unroll
-  for (int h = 0; h < R; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    f32_store<D>(tile, buf);
-    __syncthreads();
-    if (t + 1 < ntiles) f32_fetch<D>(buf, K, (t + 1) * kF32Tile, n);
-    float sc[R][kF32Tile / 4];
-    tile_scores<D, R>(q, tile, s, sc);
-#pragma unroll
-    for (int h = 0; h < R; ++h)
-#pragma unroll
-      for (int g = 0; g < kF32Tile / 4; ++g) sc[h][g] *= c;
-    if (t * kF32Tile + kF32Tile - 1 > qb * ROWS) {
+    for (int h = 0; h < R; ++h) {
+      m[h] = kNegInf;
+      l[h] = 0.f;
+    }
+    for (int t = 0; t < ntiles; ++t) {
+      __syncthreads();
+      f32_store<D>(tile, buf);
+      __syncthreads();
+      if (t + 1 < ntiles) f32_fetch<D>(buf, K, (t + 1) * kF32Tile, n);
+      float sc[R][kF32Tile / 4];
+      tile_scores<D, R>(q, tile, s, sc);
 #pragma unroll
       for (int h = 0; h < R; ++h)
 #pragma unroll
-        for (int g = 0; g < kF32Tile / 4; ++g)
-          if (t * kF32Tile + 4 * g + s > i0 + h * kF32Rows) sc[h][g] = kNegInf;
+        for (int g = 0; g < kF32Tile / 4; ++g) sc[h][g] *= c;
+      if (t * kF32Tile + kF32Tile - 1 > qb * ROWS) {
+#pragma unroll
+        for (int h = 0; h < R; ++h)
+#pragma unroll
+          for (int g = 0; g < kF32Tile / 4; ++g)
+            if (t * kF32Tile + 4 * g + s > i0 + h * kF32Rows) sc[h][g] = kNegInf;
+      }
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        float mt = sc[h][0];
+#pragma unroll
+        for (int g = 1; g < kF32Tile / 4; ++g) mt = fmaxf(mt, sc[h][g]);
+        const float mn = fmaxf(m[h], mt), ms = mn == kNegInf ? 0.f : mn;
+        float p = 0.f;
+#pragma unroll
+        for (int g = 0; g < kF32Tile / 4; ++g) p += fast_exp2(sc[h][g] - ms);
+        l[h] = fmaf(l[h], fast_exp2(m[h] - ms), p);
+        m[h] = mn;
+      }
     }
 #pragma unroll
     for (int h = 0; h < R; ++h) {
-      float mt = sc[h][0];
-#pragma unroll
-      for (int g = 1; g < kF32Tile / 4; ++g) mt = fmaxf(mt, sc[h][g]);
-      const float mn = fmaxf(m[h], mt), ms = mn == kNegInf ? 0.f : mn;
-      float p = 0.f;
-#pragma unroll
-      for (int g = 0; g < kF32Tile / 4; ++g) p += fast_exp2(sc[h][g] - ms);
-      l[h] = fmaf(l[h], fast_exp2(m[h] - ms), p);
-      m[h] = mn;
+      const int i = i0 + h * kF32Rows;
+      const float M = quad_max(m[h]);  // finite: key i lies in the row of lane i % 4
+      const float total = group_sum<4>(l[h] * fast_exp2(m[h] - M));
+      if (s == 0 && i < n) a.lse2[size_t(head) * ld_lse + i] = M + fast_log2(total);
     }
-  }
-#pragma unroll
-  for (int h = 0; h < R; ++h) {
-    const int i = i0 + h * kF32Rows;
-    const float M = quad_max(m[h]);  // finite: key i lies in the row of lane i % 4
-    const float total = group_sum<4>(l[h] * fast_exp2(m[h] - M));
-    if (s == 0 && i < n) a.lse2[size_t(head) * ld_lse + i] = M + fast_log2(total);
   }
 }
 
 // Pass 1 with output, fp32: the quad keeps one running maximum so that its
 // four lanes can accumulate their columns of the output row together.
 template <int D>
-__global__ __launch_bounds__(kF32Threads) void rowattn_f32(PrefillArgs a, int nblk, int ld_lse) {
+__global__ __launch_bounds__(kF32Threads) void rowattn_f32(PrefillArgs a, int nblk, int ld_lse, int paired) {
   using L = F32Layout<D>;
   __shared__ float4 ktile[L::TILE4];
   __shared__ float4 vtile[L::TILE4];
-  const int head = blockIdx.x / nblk;
-  const int qb = nblk - 1 - blockIdx.x % nblk;
+  const int per_head = paired ? (nblk + 1) / 2 : nblk;
+  const int head = blockIdx.x / per_head;
+  const int pr = blockIdx.x % per_head;
   const int n = a.n, s = threadIdx.x & 3;
-  const int i = qb * kF32Rows + (threadIdx.x >> 2);
   const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
   const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
   const float* V = static_cast<const float*>(a.V) + size_t(head) * n * D;
   const float c = a.c;
-  float4 q[L::C4], o[L::C4];
-  f32_row<D>(q, Q, i, n, s);
+  for (int seg = 0; seg < 2; ++seg) {  // row blocks as in rowlse_f32
+    const int qb = seg == 0 ? nblk - 1 - pr : pair_partner(nblk, pr);
+    if (seg == 1 && (!paired || qb < 0)) break;
+    const int i = qb * kF32Rows + (threadIdx.x >> 2);
+    float4 q[L::C4], o[L::C4];
+    f32_row<D>(q, Q, i, n, s);
 #pragma unroll
-  for (int e = 0; e < L::C4; ++e) o[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-  const int ntiles = (min(n, (qb + 1) * kF32Rows) + kF32Tile - 1) / kF32Tile;
-  float4 kbuf[L::LOADS], vbuf[L::LOADS];
-  f32_fetch<D>(kbuf, K, 0, n);
-  f32_fetch<D>(vbuf, V, 0, n);
-  float m = kNegInf, l = 0.f;
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    f32_store<D>(ktile, kbuf);
-    f32_store<D>(vtile, vbuf);
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      f32_fetch<D>(kbuf, K, (t + 1) * kF32Tile, n);
-      f32_fetch<D>(vbuf, V, (t + 1) * kF32Tile, n);
-    }
-    float sc[kF32Tile / 4];
+    for (int e = 0; e < L::C4; ++e) o[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int ntiles = (min(n, (qb + 1) * kF32Rows) + kF32Tile - 1) / kF32Tile;
+    float4 kbuf[L::LOADS], vbuf[L::LOADS];
+    f32_fetch<D>(kbuf, K, 0, n);
+    f32_fetch<D>(vbuf, V, 0, n);
+    float m = kNegInf, l = 0.f;
+    for (int t = 0; t < ntiles; ++t) {
+      __syncthreads();
+      f32_store<D>(ktile, kbuf);
+      f32_store<D>(vtile, vbuf);
+      __syncthreads();
+      if (t + 1 < ntiles) {
+        f32_fetch<D>(kbuf, K, (t + 1) * kF32Tile, n);
+        f32_fetch<D>(vbuf, V, (t + 1) * kF32Tile, n);
+      }
+      float sc[kF32Tile / 4];
 #pragma unroll
-    for (int g = 0; g < kF32Tile / 4; ++g) sc[g] = quad_score<D>(q, ktile, g, s) * c;
-    if (t * kF32Tile + kF32Tile - 1 > qb * kF32Rows) {
+      for (int g = 0; g < kF32Tile / 4; ++g) sc[g] = quad_score<D>(q, ktile, g, s) * c;
+      if (t * kF32Tile + kF32Tile - 1 > qb * kF32Rows) {
 #pragma unroll
-      for (int g = 0; g < kF32Tile / 4; ++g)
-        if (t * kF32Tile + 4 * g + s > i) sc[g] = kNegInf;
-    }
-    float mt = sc[0];
+        for (int g = 0; g < kF32Tile / 4; ++g)
+          if (t * kF32Tile + 4 * g + s > i) sc[g] = kNegInf;
+      }
+      float mt = sc[0];
 #pragma unroll
-    for (int g = 1; g < kF32Tile / 4; ++g) mt = fmaxf(mt, sc[g]);
-    const float mn = fmaxf(m, quad_max(mt)), ms = mn == kNegInf ? 0.f : mn;
-    const float alpha = fast_exp2(m - ms);
-    float psum = 0.f;
+      for (int g = 1; g < kF32Tile / 4; ++g) mt = fmaxf(mt, sc[g]);
+      const float mn = fmaxf(m, quad_max(mt)), ms = mn == kNegInf ? 0.f : mn;
+      const float alpha = fast_exp2(m - ms);
+      float psum = 0.f;
 #pragma unroll
-    for (int g = 0; g < kF32Tile / 4; ++g) {
-      sc[g] = fast_exp2(sc[g] - ms);
-      psum += sc[g];
-    }
-    l = fmaf(l, alpha, psum);
+      for (int g = 0; g < kF32Tile / 4; ++g) {
+        sc[g] = fast_exp2(sc[g] - ms);
+        psum += sc[g];
+      }
+      l = fmaf(l, alpha, psum);
 #pragma unroll
-    for (int e = 0; e < L::C4; ++e) {
-      o[e].x *= alpha;
-      o[e].y *= alpha;
-      o[e].z *= alpha;
-      o[e].w *= alpha;
-    }
+      for (int e = 0; e < L::C4; ++e) {
+        o[e].x *= alpha;
+        o[e].y *= alpha;
+        o[e].z *= alpha;
+        o[e].w *= alpha;
+      }
 #pragma unroll
-    for (int g = 0; g < kF32Tile / 4; ++g) {
-      const float p[4] = {quad_bcast<0>(sc[g]), quad_bcast<1>(sc[g]), quad_bcast<2>(sc[g]), quad_bcast<3>(sc[g])};
+      for (int g = 0; g < kF32Tile / 4; ++g) {
+        const float p[4] = {quad_bcast<0>(sc[g]), quad_bcast<1>(sc[g]), quad_bcast<2>(sc[g]), quad_bcast<3>(sc[g])};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float4* row = vtile + (4 * g + r) * (D / 4) + s;
+        for (int r = 0; r < 4; ++r) {
+          const float4* row = vtile + (4 * g + r) * (D / 4) + s;
 #pragma unroll
-        for (int e = 0; e < L::C4; ++e) {
-          const float4 y = row[4 * e];
-          o[e].x = fmaf(p[r], y.x, o[e].x);
-          o[e].y = fmaf(p[r], y.y, o[e].y);
-          o[e].z = fmaf(p[r], y.z, o[e].z);
-          o[e].w = fmaf(p[r], y.w, o[e].w);
+          for (int e = 0; e < L::C4; ++e) {
+            const float4 y = row[4 * e];
+            o[e].x = fmaf(p[r], y.x, o[e].x);
+            o[e].y = fmaf(p[r], y.y, o[e].y);
+            o[e].z = fmaf(p[r], y.z, o[e].z);
+            o[e].w = fmaf(p[r], y.w, o[e].w);
+          }
         }
       }
+      m = mn;
     }
-    m = mn;
-  }
-  const float total = group_sum<4>(l);
-  if (i >= n) return;
-  const float lse2 = m + fast_log2(total);
-  if (s == 0) {
-    a.lse2[size_t(head) * ld_lse + i] = lse2;
-    if (a.lse_out) a.lse_out[size_t(head) * n + i] = lse2 * 0.6931471805599453f;
-  }
-  const float inv = 1.0f / total;
-  float4* orow = reinterpret_cast<float4*>(a.out + (size_t(head) * n + i) * D);
+    const float total = group_sum<4>(l);
+    if (i < n) {  // no early return: the next row block's tiles need every thread at the barriers
+      const float lse2 = m + fast_log2(total);
+      if (s == 0) {
+        a.lse2[size_t(head) * ld_lse + i] = lse2;
+        if (a.lse_out) a.lse_out[size_t(head) * n + i] = lse2 * 0.6931471805599453f;
+      }
+      const float inv = 1.0f / total;
+      float4* orow = reinterpret_cast<float4*>(a.out + (size_t(head) * n + i) * D);
 #pragma unroll
-  for (int e = 0; e < L::C4; ++e) orow[4 * e + s] = make_float4(o[e].x * inv, o[e].y * inv, o[e].z * inv, o[e].w * inv);
+      for (int e = 0; e < L::C4; ++e) orow[4 * e + s] = make_float4(o[e].x * inv, o[e].y * inv, o[e].z * inv, o[e].w * inv);
+    }
+  }
 }
 
 // Pass 1 replaced by the caller's natural-log normalisers: lse2 = lse * log2(e).
@@ -995,69 +1008,77 @@ __global__ void lse_from_natural(PrefillArgs a, int G, int ld_lse) {
 // and streams the queries at and after its first key, with their
 // normalisers, through LDS.
 template <int D, int R>
-__global__ __launch_bounds__(kF32Threads) void colsum_f32(PrefillArgs a, int nblk, int ld_lse) {
+__global__ __launch_bounds__(kF32Threads) void colsum_f32(PrefillArgs a, int nblk, int ld_lse, int paired) {
   using L = F32Layout<D>;
   constexpr int ROWS = R * kF32Rows;  // keys per workgroup
   __shared__ float4 tile[L::TILE4];
   __shared__ float ltile[kF32Tile];
-  const int head = blockIdx.x / nblk;
-  const int kb = blockIdx.x % nblk;  // key block 0 streams the most queries
+  const int per_head = paired ? (nblk + 1) / 2 : nblk;
+  const int head = blockIdx.x / per_head;
+  const int pr = blockIdx.x % per_head;
   const int n = a.n, s = threadIdx.x & 3;
-  const int k0 = kb * ROWS, j0 = k0 + (threadIdx.x >> 2);  // keys j0 + h * kF32Rows
   const float* Q = static_cast<const float*>(a.Q) + size_t(head) * n * D;
   const float* K = static_cast<const float*>(a.K) + size_t(head) * n * D;
   const float* lse = a.lse2 + size_t(head) * ld_lse;
   const float c = a.c;
-  float4 kr[R][L::C4];
+  // Key block pr (block 0 streams the most queries), then, when paired,
+  // block nblk - 1 - pair_partner(pr) (as in colsum_lds).
+  for (int seg = 0; seg < 2; ++seg) {
+    const int partner = pair_partner(nblk, pr);
+    const int kb = seg == 0 ? pr : nblk - 1 - partner;
+    if (seg == 1 && (!paired || partner < 0)) break;
+    const int k0 = kb * ROWS, j0 = k0 + (threadIdx.x >> 2);  // keys j0 + h * kF32Rows
+    float4 kr[R][L::C4];
 #pragma unroll
-  for (int h = 0; h < R; ++h) f32_row<D>(kr[h], K, j0 + h * kF32Rows, n, s);
-  const int t0 = k0 / kF32Tile, ntiles = (n + kF32Tile - 1) / kF32Tile;
-  float4 buf[L::LOADS];
-  f32_fetch<D>(buf, Q, t0 * kF32Tile, n);
-  const int lr = threadIdx.x < kF32Tile ? t0 * kF32Tile + threadIdx.x : n;
-  float lbuf = lr < n ? lse[lr] : 0.f;
-  float sum[R], comp[R];
+    for (int h = 0; h < R; ++h) f32_row<D>(kr[h], K, j0 + h * kF32Rows, n, s);
+    const int t0 = k0 / kF32Tile, ntiles = (n + kF32Tile - 1) / kF32Tile;
+    float4 buf[L::LOADS];
+    f32_fetch<D>(buf, Q, t0 * kF32Tile, n);
+    const int lr = threadIdx.x < kF32Tile ? t0 * kF32Tile + threadIdx.x : n;
+    float lbuf = lr < n ? lse[lr] : 0.f;
+    float sum[R], comp[R];
 #pragma unroll
-  for (int h = 0; h < R; ++h) {
-    sum[h] = 0.f;
-    comp[h] = 0.f;
-  }
-  for (int t = t0; t < ntiles; ++t) {
-    __syncthreads();
-    f32_store<D>(tile, buf);
-    if (threadIdx.x < kF32Tile) ltile[threadIdx.x] = lbuf;
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      f32_fetch<D>(buf, Q, (t + 1) * kF32Tile, n);
-      const int r = threadIdx.x < kF32Tile ? (t + 1) * kF32Tile + threadIdx.x : n;
-      lbuf = r < n ? lse[r] : 0.f;
+    for (int h = 0; h < R; ++h) {
+      sum[h] = 0.f;
+      comp[h] = 0.f;
     }
-    const bool edge = t * kF32Tile < k0 + ROWS || (t + 1) * kF32Tile > n;
-    float sc[R][kF32Tile / 4];
-    tile_scores<D, R>(kr, tile, s, sc);
+    for (int t = t0; t < ntiles; ++t) {
+      __syncthreads();
+      f32_store<D>(tile, buf);
+      if (threadIdx.x < kF32Tile) ltile[threadIdx.x] = lbuf;
+      __syncthreads();
+      if (t + 1 < ntiles) {
+        f32_fetch<D>(buf, Q, (t + 1) * kF32Tile, n);
+        const int r = threadIdx.x < kF32Tile ? (t + 1) * kF32Tile + threadIdx.x : n;
+        lbuf = r < n ? lse[r] : 0.f;
+      }
+      const bool edge = t * kF32Tile < k0 + ROWS || (t + 1) * kF32Tile > n;
+      float sc[R][kF32Tile / 4];
+      tile_scores<D, R>(kr, tile, s, sc);
 #pragma unroll
-    for (int g = 0; g < kF32Tile / 4; ++g) {
-      float v[R];
+      for (int g = 0; g < kF32Tile / 4; ++g) {
+        float v[R];
 #pragma unroll
-      for (int h = 0; h < R; ++h) v[h] = sc[h][g];
-      const float lq = ltile[4 * g + s];
-      const int qi = t * kF32Tile + 4 * g + s;
+        for (int h = 0; h < R; ++h) v[h] = sc[h][g];
+        const float lq = ltile[4 * g + s];
+        const int qi = t * kF32Tile + 4 * g + s;
 #pragma unroll
-      for (int h = 0; h < R; ++h) {
-        float p = fast_exp2(fmaf(v[h], c, -lq));
-        if (edge && (qi < j0 + h * kF32Rows || qi >= n)) p = 0.f;
-        const float y = p - comp[h];
-        const float u = sum[h] + y;
-        comp[h] = (u - sum[h]) - y;
-        sum[h] = u;
+        for (int h = 0; h < R; ++h) {
+          float p = fast_exp2(fmaf(v[h], c, -lq));
+          if (edge && (qi < j0 + h * kF32Rows || qi >= n)) p = 0.f;
+          const float y = p - comp[h];
+          const float u = sum[h] + y;
+          comp[h] = (u - sum[h]) - y;
+          sum[h] = u;
+        }
       }
     }
-  }
 #pragma unroll
-  for (int h = 0; h < R; ++h) {
-    const int j = j0 + h * kF32Rows;
-    const float total = group_sum<4>(sum[h] - comp[h]);
-    if (s == 0 && j < n) a.colsum[size_t(head) * n + j] = total;
+    for (int h = 0; h < R; ++h) {
+      const int j = j0 + h * kF32Rows;
+      const float total = group_sum<4>(sum[h] - comp[h]);
+      if (s == 0 && j < n) a.colsum[size_t(head) * n + j] = total;
+    }
   }
 }
 
@@ -1332,18 +1353,20 @@ hipError_t prefill_typed(int G, const PrefillArgs& a, hipStream_t s) {
     // workgroups; below that, one row keeps the workgroup count up.
     const bool two = int64_t(G) * a.n >= kF32TwoRowsMin;
     const int nblk2 = (a.n + 2 * kF32Rows - 1) / (2 * kF32Rows);
+    const int p1 = pair_blocks(nblk), p2 = pair_blocks(nblk2);
+    const int wg1 = p1 ? (nblk + 1) / 2 : nblk, wg2 = p2 ? (nblk2 + 1) / 2 : nblk2;  // workgroups per head
     if (a.pass1 == PASS1_LSE) {
       if (two)
-        hipLaunchKernelGGL((rowlse_f32<D, 2>), dim3(G * nblk2), dim3(kF32Threads), 0, s, a, nblk2, ld_lse);
+        hipLaunchKernelGGL((rowlse_f32<D, 2>), dim3(G * wg2), dim3(kF32Threads), 0, s, a, nblk2, ld_lse, p2);
       else
-        hipLaunchKernelGGL((rowlse_f32<D, 1>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
+        hipLaunchKernelGGL((rowlse_f32<D, 1>), dim3(G * wg1), dim3(kF32Threads), 0, s, a, nblk, ld_lse, p1);
     } else if (a.pass1 == PASS1_ATTENTION) {
-      hipLaunchKernelGGL((rowattn_f32<D>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
+      hipLaunchKernelGGL((rowattn_f32<D>), dim3(G * wg1), dim3(kF32Threads), 0, s, a, nblk, ld_lse, p1);
     }
     if (two)
-      hipLaunchKernelGGL((colsum_f32<D, 2>), dim3(G * nblk2), dim3(kF32Threads), 0, s, a, nblk2, ld_lse);
+      hipLaunchKernelGGL((colsum_f32<D, 2>), dim3(G * wg2), dim3(kF32Threads), 0, s, a, nblk2, ld_lse, p2);
     else
-      hipLaunchKernelGGL((colsum_f32<D, 1>), dim3(G * nblk), dim3(kF32Threads), 0, s, a, nblk, ld_lse);
+      hipLaunchKernelGGL((colsum_f32<D, 1>), dim3(G * wg1), dim3(kF32Threads), 0, s, a, nblk, ld_lse, p1);
   } else {
     const int nblk = (a.n + 255) / 256;
     if (a.pass1 == PASS1_ATTENTION) {
