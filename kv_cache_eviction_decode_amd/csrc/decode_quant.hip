@@ -90,21 +90,26 @@ __global__ __launch_bounds__(64, 2) void decode_quant_kernel(DecodeArgs a, int G
     }
     // The head's first batch of codes goes out right behind its inputs, so
     // that its latency overlaps the folding of q and the quantisation below.
-    const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * RB + sub * CB;
-    const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * RB + sub * CB;
+    const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * RB;
+    const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * RB;
     const float2* vg = reinterpret_cast<const float2*>(a.v_qparam) + hrow;
-    // Loads are unconditional (clamped to the last occupied row, masked; slot
-    // 0 when the cache is empty, whose values are then never used) so that
-    // the compiler's wait counts stay exact: a conditional first batch makes
-    // it wait for every load before the quantisation below.
-    const int last = max(nu - 1, 0);
+    // Loads are unconditional (rows past the occupied ones read as zeros,
+    // range-checked by the buffer load, and are masked) so that the
+    // compiler's wait counts stay exact: a conditional first batch makes it
+    // wait for every load before the quantisation below. A batch's offsets
+    // are one vector add from the lane's constant; each unit's is an
+    // immediate on top.
+    const auto Kr = rows_rsrc(Kh, nu * RB);
+    const auto Vr = rows_rsrc(Vh, nu * RB);
+    const auto Gr = rows_rsrc(vg, nu * 8);
+    const uint32_t lane_off = uint32_t(grp * RB + sub * CB), lane_goff = uint32_t(grp * 8);
     auto issue = [&](CT (&kb)[UB], CT (&vb)[UB], float2 (&gb)[UB], int b) {
+      const uint32_t off = lane_off + uint32_t(b * UB * RPU * RB), goff = lane_goff + uint32_t(b * UB * RPU * 8);
 #pragma unroll
       for (int j = 0; j < UB; ++j) {
-        const int row = min((b * UB + j) * RPU + grp, last);
-        kb[j] = LC::load(Kh + size_t(row) * RB);
-        vb[j] = LC::load(Vh + size_t(row) * RB);
-        gb[j] = vg[row];
+        kb[j] = LC::load(Kr, off + j * RPU * RB);
+        vb[j] = LC::load(Vr, off + j * RPU * RB);
+        gb[j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(Gr, goff + j * RPU * 8, 0, 0));
       }
     };
     CT kA[UB], vA[UB], kB[UB], vB[UB];
@@ -423,8 +428,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void decode_quant_wg_kernel(DecodeAr
   }
 
   // ---- stream this wave's rows -------------------------------------------------------
-  const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * RB + sub * CB;
-  const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * RB + sub * CB;
+  const uint8_t* Kh = static_cast<const uint8_t*>(a.K) + hrow * RB;
+  const uint8_t* Vh = static_cast<const uint8_t*>(a.V) + hrow * RB;
   const float2* vg = reinterpret_cast<const float2*>(a.v_qparam) + hrow;
   float m = kNegInf, l = 0.f, pm = 0.f;
   float acc[16];
@@ -433,13 +438,20 @@ __global__ __launch_bounds__(WAVES * 64, 2) void decode_quant_wg_kernel(DecodeAr
   const int units = (nu + RPU - 1) / RPU;
   const int nb = (units + WAVES * UB - 1) / (WAVES * UB);  // batches per wave
   auto row_of = [&](int b, int j) { return ((b * UB + j) * WAVES + wave) * RPU + grp; };
+  // As in the wave kernel: the head's rows as buffer resources (rows past
+  // the occupied ones read as zeros), one vector add per batch.
+  const int lrow = wave * RPU + grp;  // the lane's row within a unit of WAVES waves
+  const auto Kr = rows_rsrc(Kh, nu * RB);
+  const auto Vr = rows_rsrc(Vh, nu * RB);
+  const auto Gr = rows_rsrc(vg, nu * 8);
+  const uint32_t lane_off = uint32_t(lrow * RB + sub * CB), lane_goff = uint32_t(lrow * 8);
   auto issue = [&](CT (&kb)[UB], CT (&vb)[UB], float2 (&gb)[UB], int b) {
+    const uint32_t off = lane_off + uint32_t(b * UB * WAVES * RPU * RB), goff = lane_goff + uint32_t(b * UB * WAVES * RPU * 8);
 #pragma unroll
     for (int j = 0; j < UB; ++j) {
-      const int row = min(row_of(b, j), nu - 1);
-      kb[j] = LC::load(Kh + size_t(row) * RB);
-      vb[j] = LC::load(Vh + size_t(row) * RB);
-      gb[j] = vg[row];
+      kb[j] = LC::load(Kr, off + j * WAVES * RPU * RB);
+      vb[j] = LC::load(Vr, off + j * WAVES * RPU * RB);
+      gb[j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(Gr, goff + j * WAVES * RPU * 8, 0, 0));
     }
   };
   auto compute = [&](const CT (&kb)[UB], const CT (&vb)[UB], const float2 (&gb)[UB], int b) {

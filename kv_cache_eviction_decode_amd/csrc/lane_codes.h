@@ -7,6 +7,16 @@
 
 namespace h2o {
 
+// Rows of codes (or of value grids) from `base` on as a raw buffer resource
+// holding `bytes` bytes (>= 0): a load at or past that count returns zeros,
+// range-checked by the load itself, so rows past the occupied ones need no
+// clamp. The base must be the same in every lane (scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int bytes) {
+  constexpr int kWord3 = 0x00020000;  // gfx9-family raw buffer: 32-bit data format, no swizzle
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes > 0 ? bytes : 0, kWord3);
+}
+constexpr int kLoadNT = 2;  // cache-policy bit of a non-temporal buffer load
+
 // A value the compiler must treat as opaque: keeps a masked code word from
 // being folded into one bit-field extract per code, so that each code is
 // converted by a single v_cvt_f32_ubyteN of its byte.
@@ -24,6 +34,9 @@ template <> struct LaneCodes<8> {
   using T = uint4;
   __device__ __forceinline__ static constexpr float inv_weight(int) { return 1.0f; }
   __device__ __forceinline__ static T load(const uint8_t* p) { return ldnt16(p); }
+  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadNT));
+  }
   __device__ __forceinline__ static void store(uint8_t* p, T v) { *reinterpret_cast<uint4*>(p) = v; }
   __device__ __forceinline__ static void to_float(T w, float (&c)[16]) {
     const uint32_t v[4] = {w.x, w.y, w.z, w.w};
@@ -42,6 +55,9 @@ template <> struct LaneCodes<8> {
 template <> struct LaneCodes<4> {
   using T = uint2;
   __device__ __forceinline__ static T load(const uint8_t* p) { return ldnt8(p); }
+  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadNT));
+  }
   __device__ __forceinline__ static void store(uint8_t* p, T v) { *reinterpret_cast<uint2*>(p) = v; }
   // Word i holds channels 8i..8i+7; masking the low and the high nibbles
   // in place leaves the even channels one per byte and the odd ones one per
@@ -69,6 +85,9 @@ template <> struct LaneCodes<4> {
 template <> struct LaneCodes<2> {
   using T = uint32_t;
   __device__ __forceinline__ static T load(const uint8_t* p) { return ldnt4(p); }
+  __device__ __forceinline__ static T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadNT);
+  }
   __device__ __forceinline__ static void store(uint8_t* p, T v) { *reinterpret_cast<uint32_t*>(p) = v; }
   // Byte b holds channels 4b..4b+3; the j-th crumb of every byte is channel
   // 4b + j, masked in place: one per byte times 4^j (weight 4^(i mod 4)).
