@@ -445,13 +445,24 @@ __global__ __launch_bounds__(WAVES * 64, 2) void decode_quant_wg_kernel(DecodeAr
   const auto Vr = rows_rsrc(Vh, nu * RB);
   const auto Gr = rows_rsrc(vg, nu * 8);
   const uint32_t lane_off = uint32_t(lrow * RB + sub * CB), lane_goff = uint32_t(lrow * 8);
+  // 8- and 4-bit codes keep pointer loads clamped to the last occupied row:
+  // at 256 heads x 2048 slots the buffer form measured 8 bits 27.38 -> 27.80
+  // us and 4 bits 20.83 -> 21.32 us, against 2 bits 18.26 -> 17.35 us.
+  constexpr bool kBufferRows = BITS == 2;
   auto issue = [&](CT (&kb)[UB], CT (&vb)[UB], float2 (&gb)[UB], int b) {
     const uint32_t off = lane_off + uint32_t(b * UB * WAVES * RPU * RB), goff = lane_goff + uint32_t(b * UB * WAVES * RPU * 8);
 #pragma unroll
     for (int j = 0; j < UB; ++j) {
-      kb[j] = LC::load(Kr, off + j * WAVES * RPU * RB);
-      vb[j] = LC::load(Vr, off + j * WAVES * RPU * RB);
-      gb[j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(Gr, goff + j * WAVES * RPU * 8, 0, 0));
+      if constexpr (kBufferRows) {
+        kb[j] = LC::load(Kr, off + j * WAVES * RPU * RB);
+        vb[j] = LC::load(Vr, off + j * WAVES * RPU * RB);
+        gb[j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(Gr, goff + j * WAVES * RPU * 8, 0, 0));
+      } else {
+        const int row = min(row_of(b, j), nu - 1);
+        kb[j] = LC::load(Kh + size_t(row) * RB + sub * CB);
+        vb[j] = LC::load(Vh + size_t(row) * RB + sub * CB);
+        gb[j] = vg[row];
+      }
     }
   };
   auto compute = [&](const CT (&kb)[UB], const CT (&vb)[UB], const float2 (&gb)[UB], int b) {
