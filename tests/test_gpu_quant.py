@@ -75,6 +75,20 @@ def test_quant_wave_kernel_beyond_prefetch(gpu, quant):
 
 
 @pytest.mark.parametrize("quant", FORMATS)
+def test_quant_wave_kernel_filling(gpu, quant):
+    """1024 heads (one wave per head) whose cache fills during decode: a
+    100-token prompt into 161 slots, so the occupied count (100 to 161) ends
+    inside a batch of rows at every step and the rows past it must read as
+    nothing, then 9 steps with the cache full."""
+    wl = Workload("quant_wave_filling", 32, 32, 128, "bf16", 100, 81, 80, 70, 1.5, 0.0, 57)
+    run = ParityRun(wl, wl.steps, sample=sample_heads(wl, 8), quant=quant)
+    run.prefill()
+    rep = run.decode()
+    log(f"[{quant}] wave kernel, cache filling: {rep}")
+    assert rep.steps == wl.steps
+
+
+@pytest.mark.parametrize("quant", FORMATS)
 def test_quant_uniform_closed_form_full_shape(gpu, quant):
     """All-zero queries at the OPT-6.7B layer shape over a cache of codes:
     every logit is 0 whatever the key codes, so the column sums are harmonic
