@@ -105,6 +105,18 @@ def test_max_slots(gpu):
     log(f"[parity] max_slots: {rep}")
 
 
+def test_max_slots_wave_kernel(gpu):
+    """1024 heads of 8192 slots, the largest cache, through the
+    one-wave-per-head kernel (its 8192 logits take 32 KiB of a workgroup's
+    LDS); 4 sampled heads over 4 steps, every step with a full cache."""
+    wl = Workload("max_slots_1024", 8, 128, 128, "bf16", 8300, 4096, 4096, 4, 1.5, 0.0, 33)
+    run = ParityRun(wl, wl.steps, sample=sample_heads(wl, 4))
+    run.prefill()
+    rep = run.decode()
+    log(f"[parity] max slots, 1024 heads: {rep}")
+    assert rep.steps == wl.steps
+
+
 def test_wave_kernel_beyond_prefetch(gpu):
     """1024 heads (the one-wave-per-head kernel) with 640 slots: scores and
     positions past the 512 prefetched per head are read in the epilogue."""

@@ -89,6 +89,29 @@ def test_quant_wave_kernel_filling(gpu, quant):
 
 
 @pytest.mark.parametrize("quant", FORMATS)
+def test_quant_max_slots(gpu, quant):
+    """The largest cache, 8192 slots of codes, for two heads (the
+    workgroup-per-head kernel) over 4 steps with the cache full."""
+    wl = Workload("quant_max_slots", 1, 2, 128, "bf16", 8300, 4096, 4096, 4, 1.5, 0.0, 35)
+    run = ParityRun(wl, wl.steps, quant=quant)
+    run.prefill()
+    rep = run.decode()
+    log(f"[{quant}] max slots, 2 heads: {rep}")
+    assert rep.steps == wl.steps
+
+
+def test_quant_max_slots_wave_kernel(gpu):
+    """8192 slots of 4-bit codes for 1024 heads (the one-wave-per-head
+    kernel, 32 KiB of logits in LDS); 4 sampled heads over 4 steps."""
+    wl = Workload("quant_max_slots_1024", 8, 128, 128, "bf16", 8300, 4096, 4096, 4, 1.5, 0.0, 36)
+    run = ParityRun(wl, wl.steps, sample=sample_heads(wl, 4), quant="u4")
+    run.prefill()
+    rep = run.decode()
+    log(f"[u4] max slots, 1024 heads: {rep}")
+    assert rep.steps == wl.steps
+
+
+@pytest.mark.parametrize("quant", FORMATS)
 def test_quant_uniform_closed_form_full_shape(gpu, quant):
     """All-zero queries at the OPT-6.7B layer shape over a cache of codes:
     every logit is 0 whatever the key codes, so the column sums are harmonic
